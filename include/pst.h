@@ -1,0 +1,274 @@
+/*
+ * pst.h -- prefix-shared tree decode attention on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpst.so.  Plain pointers and sizes only; no C++ or framework
+ * types cross it.  Streams are passed as `void*` and mean a hipStream_t
+ * (NULL = the device's null stream).
+ *
+ * What the library computes.  A batch of decode queries sits on a forest of
+ * KV-cache nodes joined under a virtual root; each edge p -> c says p's
+ * tokens are the prefix of c's (CoDec: Prefix-Shared Decoding Kernel for
+ * LLMs, section KV缓存管理 / KV-cache management).  Query r and q-head h
+ * attend, with one softmax, to every token of every node on the path from
+ * the root to the query's node (for a masked node, to the tokens whose bit
+ * is set in the query's 64-bit mask: the bit causal mask of DEFT: Decoding
+ * with Flash Tree-Attention, section 3.3 / Table 2):
+ *     O[r,h] = softmax(scale * q[r,h] K_vis^T) V_vis,
+ *     LSE[r,h] = ln sum exp(scale * q[r,h] K_vis^T).
+ * It does so the way CoDec's kernel executor does (section 块内内核原语 and
+ * 块间启动与树归约): one partial-attention (PAC) pass reads each node's K/V
+ * once for all the queries whose path contains it and writes a normalised
+ * partial output plus its LSE per (query, node piece); one partial-output
+ * reduction (POR) pass merges each query's partials along an independent
+ * chain.  Pieces and their assignment to workgroups come from a host plan
+ * that balances a fitted per-piece cost C_est(rows, length) (section
+ * 工作负载平衡 / workload balance).
+ *
+ * Conventions.
+ *   g = num_q_heads / num_kv_heads; q-head h reads kv head h / g.
+ *   Q   [num_queries][num_q_heads][head_dim], contiguous, in_dtype.
+ *   K,V pools: element (kv head a, token t, channel c) at
+ *       a * kv_stride_head + t * kv_stride_token + c      (elements, in_dtype)
+ *       (default: head-major [num_kv_heads][pool_tokens][head_dim]).
+ *   out [num_queries][num_q_heads][head_dim], contiguous, out_dtype.
+ *   lse_out [num_queries][num_q_heads] float32, natural log (optional).
+ *   Every pointer passed to pst_decode_attn / pst_pac / pst_por is device
+ *   memory owned by the caller; the library never frees it.
+ *
+ * Errors.  Every entry point returns a pst_status; on failure
+ * pst_last_error() returns a thread-local message.  Argument, tree and
+ * staleness checks are synchronous.  Kernel launches are asynchronous on the
+ * given stream; a launch failure returns PST_E_HIP, a fault in a kernel
+ * surfaces at the caller's next synchronisation.
+ *
+ * Lifetime.  The library owns trees, plans and cost models (and the device
+ * copies of their index arrays); pst_free releases them.  A plan borrows its
+ * tree: free plans before their tree (freeing a tree with live plans returns
+ * PST_E_INVALID_ARG).  Synchronise the stream before freeing anything a
+ * launched kernel may still read.
+ */
+#ifndef PST_H
+#define PST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PST_OK = 0,
+  PST_E_INVALID_ARG = 1,   /* null pointer, bad size, bad option */
+  PST_E_INVALID_TREE = 2,  /* tree description violates the rules of pst_tree_build */
+  PST_E_UNSUPPORTED = 3,   /* dtype / head_dim / head ratio not supported */
+  PST_E_OOM = 4,           /* a host or device allocation failed */
+  PST_E_PLAN_STALE = 5,    /* plan no longer matches its tree */
+  PST_E_WORKSPACE = 6,     /* workspace missing or too small */
+  PST_E_HIP = 7,           /* a HIP runtime call failed */
+  PST_E_NO_DEVICE = 8      /* a device operation was asked of a host-only object */
+} pst_status;
+
+typedef enum { PST_F32 = 0, PST_BF16 = 1 } pst_dtype;
+
+typedef struct pst_tree_s* pst_tree_t;
+typedef struct pst_plan_s* pst_plan_t;
+typedef struct pst_cost_s* pst_cost_model_t;
+
+/* Tree description.  All arrays are host memory, read during the call and
+ * copied; the caller keeps ownership.
+ *   parent[i]      in [-1, i): the node whose tokens precede node i's; -1 =
+ *                  child of the virtual root.  Parents come before children.
+ *   kv_offset[i]   >= 0: first token of node i in the K/V pools.
+ *   kv_len[i]      >= 1: tokens in node i.
+ *   query_node[r]  in [0, num_nodes): the deepest node on query r's path.
+ *   node_masked    NULL or [num_nodes]: 1 = node i is masked (kv_len <= 64).
+ *   query_mask     NULL or [num_queries]: for a query whose own node is
+ *                  masked, bit j set = token j of that node visible.  Ignored
+ *                  for queries on unmasked nodes.  Ancestors of a query's
+ *                  node are always visible in full.
+ * Every query must see at least one token. */
+typedef struct {
+  int32_t num_nodes;
+  const int32_t* parent;
+  const int64_t* kv_offset;
+  const int32_t* kv_len;
+  int32_t num_queries;
+  const int32_t* query_node;
+  const uint64_t* query_mask;
+  const uint8_t* node_masked;
+} pst_tree_desc;
+
+/* Head layout and dtypes.  head_dim in {64, 128}; num_q_heads a multiple of
+ * num_kv_heads; in_dtype PST_F32 or PST_BF16; out_dtype PST_F32 or in_dtype.
+ * scale <= 0 means 1/sqrt(head_dim).  Strides in elements; 0 selects the
+ * head-major default.  pool_tokens = tokens per head in each pool (0 = the
+ * largest kv_offset + kv_len); every node must lie inside it. */
+typedef struct {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t in_dtype;
+  int32_t out_dtype;
+  float scale;
+  int64_t kv_stride_head;
+  int64_t kv_stride_token;
+  int64_t pool_tokens;
+} pst_shape;
+
+/* pst_tree_build flags */
+#define PST_TREE_HOST_ONLY 1u /* build and validate the index on the host only (no GPU needed) */
+
+/* Validate a tree and build its index: the node table (offset, length,
+ * number of queries through the node, depth), the query->node CSR (each
+ * query's path, root first) and the node->query CSR (each node's queries in
+ * ascending id, with the 64-bit visibility mask of each entry: the query's
+ * mask where the node is the query's own masked node, else all ones).  This
+ * is CoDec's query<->KV index (section KV缓存管理) and DEFT's QMapKV / KVMapQ
+ * (section A.8, Algorithm 1).  Unless PST_TREE_HOST_ONLY, the node table and
+ * the node->query CSR are copied to the current device on `stream` (the call
+ * returns after the copy).  On error *out is set to NULL. */
+pst_status pst_tree_build(const pst_tree_desc* desc, const pst_shape* shape, uint32_t flags,
+                          void* stream, pst_tree_t* out);
+
+/* Decode-step growth: new lengths for every node, each >= the current one
+ * (masked nodes stay <= 64).  Plans made from this tree stay valid: a node's
+ * last piece simply grows.  Uploads the lengths on `stream`. */
+pst_status pst_tree_set_lengths(pst_tree_t tree, const int32_t* kv_len, void* stream);
+
+/* Host views of the index, valid until the tree is freed. */
+typedef struct {
+  int32_t num_nodes;
+  int32_t num_queries;
+  int64_t num_entries;      /* sum over queries of path length */
+  const int32_t* depth;     /* [num_nodes] nodes from the virtual root's child, >= 1 */
+  const int32_t* n_q;       /* [num_nodes] queries whose path contains the node */
+  const int32_t* qn_ptr;    /* [num_queries + 1] */
+  const int32_t* qn_idx;    /* [num_entries] */
+  const int32_t* nq_ptr;    /* [num_nodes + 1] */
+  const int32_t* nq_idx;    /* [num_entries] */
+  const uint64_t* nq_mask;  /* [num_entries] */
+  const int64_t* visible;   /* [num_queries] tokens each query sees */
+} pst_index_view;
+pst_status pst_tree_get_index(pst_tree_t tree, pst_index_view* view);
+
+/* Cost model C_est(rows, len) in integer nanoseconds: the time one
+ * workgroup takes for one piece of `len` tokens and `rows` query rows (CoDec
+ * section 工作负载平衡: profiled over a grid, interpolated elsewhere).  The
+ * table is row-major [n_rows][n_len] over ascending grids, >= 1 everywhere and
+ * non-decreasing along both axes.  Lookup: rows -> smallest grid point >=
+ * rows (last point beyond the grid); len -> the first point's value below the
+ * grid, integer linear interpolation inside it, linear extrapolation from the
+ * last two points above it.  Arrays are copied. */
+pst_status pst_cost_model_create(int32_t n_rows, const int32_t* rows_grid, int32_t n_len,
+                                 const int32_t* len_grid, const int64_t* table, pst_cost_model_t* out);
+pst_status pst_cost_model_lookup(pst_cost_model_t cost, int32_t rows, int64_t len, int64_t* ns);
+
+/* pst_plan options (zero-initialise for defaults) */
+#define PST_PLAN_QUERY_GUIDED 1u /* FlashDecoding-style baseline: one query per row group (shared KV re-read per query) */
+#define PST_PLAN_NO_SPLIT 2u     /* every node is one piece (b_k = 1) */
+#define PST_PLAN_HOST_ONLY 4u    /* compute on the host only (no GPU needed) */
+typedef struct {
+  int32_t num_bins;    /* workgroups per kv head; 0 = resident capacity / num_kv_heads */
+  int32_t max_rows;    /* rows one workgroup holds (R_max); 0 = 256 (bf16) or 16 (f32); <= 256 */
+  int32_t tile;        /* piece granularity G in tokens; 0 = 64; a multiple of 64 */
+  int32_t grid_steps;  /* K of the grid search; 0 = 8 */
+  int32_t fixed_chunk; /* > 0: every node cut into pieces of this many tokens (ablation) */
+  uint32_t flags;
+} pst_plan_opts;
+
+/* Partition the tree's partial attention into pieces and assign them to
+ * num_bins workgroups per kv head, minimising the largest workgroup cost
+ * (CoDec section 工作负载平衡 and the min-max objective of section 速读):
+ *  1. rows of node i: r_i = n_q[i] * g; cut into ceil(r_i / R_max) row
+ *     groups of ceil(r_i / groups) rows when above R_max;
+ *  2. b pieces of node i: Lp = roundup(ceil(n_i / b), G), pieces of Lp tokens;
+ *  3. b_i(T): smallest b whose longest piece of the largest row group costs
+ *     <= T; W(T) = total cost with b_i(T);
+ *  4. cost_l: smallest T with num_bins * T >= W(T), by binary search;
+ *  5. b_i <= ceil(C_est(rows_i, n_i) / cost_l);
+ *  6. grid search over T_k = cost_l + cost_l * k / K, each candidate placed by
+ *     longest-processing-time list scheduling (ties: lowest bin id); keep the
+ *     smallest makespan (ties: fewer pieces, then smaller k).
+ * `cost` NULL selects a built-in analytic model.  The plan keeps a pointer
+ * to the tree.  Unless PST_PLAN_HOST_ONLY, the plan is copied to the device
+ * on `stream` (returns after the copy).  Integer arithmetic throughout: the
+ * same inputs give the same plan on every host. */
+pst_status pst_plan(pst_tree_t tree, pst_cost_model_t cost, const pst_plan_opts* opts, void* stream,
+                    pst_plan_t* out);
+
+/* Bytes of device workspace pst_decode_attn needs: the partial outputs
+ * [num_slots][num_q_heads][head_dim] float32 plus their LSE
+ * [num_slots][num_q_heads] float32, 256-byte aligned. */
+pst_status pst_plan_workspace_size(pst_plan_t plan, size_t* bytes);
+
+/* Host views of a plan (bit-exact comparisons, introspection). */
+#define PST_TASK_FIELDS 8 /* node, piece, kv_begin, kv_len, row_begin, row_count, flags, reserved */
+#define PST_TASK_LAST_PIECE 1
+typedef struct {
+  int32_t num_bins;
+  int32_t num_tasks;
+  int32_t num_queries;
+  int32_t num_nodes;
+  int64_t num_slots;
+  int64_t num_entries;
+  const int32_t* tasks;          /* [num_tasks][PST_TASK_FIELDS], bin-major, assignment order */
+  const int32_t* bin_ptr;        /* [num_bins + 1] */
+  const int64_t* slot_ptr;       /* [num_queries + 1] */
+  const int64_t* entry_slot;     /* [num_entries] first slot of each node->query entry */
+  const int32_t* piece_len;      /* [num_nodes] Lp (0 for nodes no query passes) */
+  const int32_t* b_eff;          /* [num_nodes] pieces per node */
+  const int32_t* rows_per_group; /* [num_nodes] */
+  const int64_t* bin_load;       /* [num_bins] estimated ns */
+  int64_t makespan;              /* estimated ns of the slowest bin */
+  int64_t cost_l;                /* binary-search bound (0 for fixed geometries) */
+  int32_t chosen_k;
+  int32_t max_rows;
+} pst_plan_view;
+pst_status pst_plan_get(pst_plan_t plan, pst_plan_view* view);
+
+/* The hot path: PAC then POR on `stream`.
+ *   q        device, [B][H_q][d] in_dtype
+ *   k_pool   device, in_dtype, layout from pst_shape
+ *   v_pool   device, in_dtype, same layout as k_pool
+ *   out      device, [B][H_q][d] out_dtype
+ *   lse_out  device [B][H_q] float32, or NULL
+ *   workspace device, >= pst_plan_workspace_size bytes, 256-byte aligned
+ * Returns PST_E_PLAN_STALE if the tree was rebuilt under the plan,
+ * PST_E_WORKSPACE if the workspace is missing or short, PST_E_NO_DEVICE for
+ * host-only objects. */
+pst_status pst_decode_attn(pst_plan_t plan, const void* q, const void* k_pool, const void* v_pool,
+                           void* out, float* lse_out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* The two launches of pst_decode_attn, separately (for per-phase timing).
+ * pst_pac writes the partials into the workspace; pst_por merges them into
+ * out / lse_out.  pst_por must follow pst_pac on the same stream. */
+pst_status pst_pac(pst_plan_t plan, const void* q, const void* k_pool, const void* v_pool,
+                   void* workspace, size_t workspace_bytes, void* stream);
+pst_status pst_por(pst_plan_t plan, void* out, float* lse_out, const void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Release a tree, plan or cost model.  NULL is accepted. */
+pst_status pst_free(void* obj);
+
+/* Thread-local message of the last failure in this thread ("" if none). */
+const char* pst_last_error(void);
+
+/* Device facts the planner uses: compute units and resident PAC workgroups
+ * per compute unit on the current device. */
+pst_status pst_device_info(int32_t* num_cu, int32_t* pac_blocks_per_cu);
+
+/* Measurement helpers (not part of the attention).
+ * pst_bench_flush: overwrite `bytes` of device memory at `buf` so that the
+ * L2 and last-level caches hold nothing the next kernel reads.
+ * pst_bench_read: read `bytes` (a multiple of 16) at `buf` with 128-bit loads
+ * and write one float per workgroup into `sink` (>= 4096 floats): the
+ * achievable HBM read bandwidth. */
+pst_status pst_bench_flush(void* buf, size_t bytes, void* stream);
+pst_status pst_bench_read(const void* buf, size_t bytes, float* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PST_H */

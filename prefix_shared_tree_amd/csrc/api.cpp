@@ -1,0 +1,659 @@
+// C ABI of libpst (see include/pst.h): object lifetimes, argument checks,
+// device uploads of the tree index and the plan, and the two launches of the
+// hot path (PAC, then POR).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "pst_internal.h"
+
+namespace pst {
+
+static thread_local std::string g_last_error;
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+// PST_FAULT_INJECT=alloc:N makes the N-th device allocation of the process
+// fail (1-based), so error paths can be tested from the host.
+static int g_alloc_count = 0;
+static bool inject_alloc_failure() {
+  static int target = [] {
+    const char* s = std::getenv("PST_FAULT_INJECT");
+    if (!s || std::strncmp(s, "alloc:", 6) != 0) return 0;
+    return std::atoi(s + 6);
+  }();
+  ++g_alloc_count;
+  return target > 0 && g_alloc_count == target;
+}
+
+static pst_status hip_fail(const char* what, hipError_t e) {
+  set_error(std::string(what) + ": " + hipGetErrorString(e));
+  return PST_E_HIP;
+}
+
+template <typename T>
+static pst_status dev_upload(T** dst, const T* src, size_t count, hipStream_t s) {
+  *dst = nullptr;
+  const size_t bytes = std::max<size_t>(count, 1) * sizeof(T);
+  if (inject_alloc_failure()) {
+    set_error("injected device allocation failure");
+    return PST_E_OOM;
+  }
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(dst), bytes);
+  if (e != hipSuccess) {
+    *dst = nullptr;
+    (void)hipGetLastError();
+    set_error(std::string("hipMalloc failed: ") + hipGetErrorString(e));
+    return PST_E_OOM;
+  }
+  if (count) {
+    e = hipMemcpyAsync(*dst, src, count * sizeof(T), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail("hipMemcpyAsync", e);
+  }
+  return PST_OK;
+}
+
+template <typename T>
+static void dev_free(T*& p) {
+  if (p) (void)hipFree(p);
+  p = nullptr;
+}
+
+}  // namespace pst
+
+using namespace pst;
+
+struct pst_tree_s {
+  uint32_t magic = kTreeMagic;
+  TreeIndex ix;
+  pst_shape shape{};
+  int64_t pool_tokens = 0;
+  bool on_device = false;
+  int device = -1;
+  uint64_t generation = 0;  // bumped when the device index is rebuilt
+  int live_plans = 0;
+  int64_t* d_node_off = nullptr;
+  int32_t* d_node_len = nullptr;
+  uint8_t* d_node_masked = nullptr;
+  int32_t* d_nq_ptr = nullptr;
+  int32_t* d_nq_idx = nullptr;
+  uint64_t* d_nq_mask = nullptr;
+};
+
+struct pst_plan_s {
+  uint32_t magic = kPlanMagic;
+  pst_tree_s* tree = nullptr;
+  uint64_t generation = 0;
+  PlanOptions opts;
+  PlanResult r;
+  bool on_device = false;
+  Task* d_tasks = nullptr;
+  int32_t* d_bin_ptr = nullptr;
+  int32_t* d_entry_slot = nullptr;
+  int64_t* d_slot_ptr = nullptr;
+};
+
+struct pst_cost_s {
+  uint32_t magic = kCostMagic;
+  CostModel model;
+};
+
+static void free_tree_device(pst_tree_s* t) {
+  dev_free(t->d_node_off);
+  dev_free(t->d_node_len);
+  dev_free(t->d_node_masked);
+  dev_free(t->d_nq_ptr);
+  dev_free(t->d_nq_idx);
+  dev_free(t->d_nq_mask);
+  t->on_device = false;
+}
+
+static void free_plan_device(pst_plan_s* p) {
+  dev_free(p->d_tasks);
+  dev_free(p->d_bin_ptr);
+  dev_free(p->d_entry_slot);
+  dev_free(p->d_slot_ptr);
+  p->on_device = false;
+}
+
+static int elem_bytes(int dt) { return dt == PST_F32 ? 4 : 2; }
+
+static pst_status check_shape(const pst_shape& s) {
+  if (s.num_q_heads < 1 || s.num_kv_heads < 1 || s.num_q_heads % s.num_kv_heads != 0) {
+    set_error("num_q_heads must be a positive multiple of num_kv_heads");
+    return PST_E_UNSUPPORTED;
+  }
+  if (s.num_q_heads / s.num_kv_heads > kMaxRows) {
+    set_error("GQA group larger than 256");
+    return PST_E_UNSUPPORTED;
+  }
+  if (s.head_dim != 64 && s.head_dim != 128) {
+    set_error("head_dim must be 64 or 128");
+    return PST_E_UNSUPPORTED;
+  }
+  if (s.in_dtype != PST_F32 && s.in_dtype != PST_BF16) {
+    set_error("in_dtype must be PST_F32 or PST_BF16");
+    return PST_E_UNSUPPORTED;
+  }
+  if (s.out_dtype != PST_F32 && s.out_dtype != s.in_dtype) {
+    set_error("out_dtype must be PST_F32 or in_dtype");
+    return PST_E_UNSUPPORTED;
+  }
+  if (s.kv_stride_head < 0 || s.kv_stride_token < 0 || s.pool_tokens < 0) {
+    set_error("negative stride or pool size");
+    return PST_E_INVALID_ARG;
+  }
+  return PST_OK;
+}
+
+extern "C" {
+
+const char* pst_last_error(void) { return g_last_error.c_str(); }
+
+pst_status pst_tree_build(const pst_tree_desc* desc, const pst_shape* shape, uint32_t flags, void* stream,
+                          pst_tree_t* out) {
+  if (!out) {
+    set_error("out is NULL");
+    return PST_E_INVALID_ARG;
+  }
+  *out = nullptr;
+  if (!desc || !shape) {
+    set_error("desc or shape is NULL");
+    return PST_E_INVALID_ARG;
+  }
+  pst_status st = check_shape(*shape);
+  if (st != PST_OK) return st;
+  pst_tree_s* t = new (std::nothrow) pst_tree_s();
+  if (!t) {
+    set_error("host allocation failed");
+    return PST_E_OOM;
+  }
+  st = build_tree_index(*desc, &t->ix);
+  if (st != PST_OK) {
+    delete t;
+    return st;
+  }
+  t->shape = *shape;
+  if (t->shape.scale <= 0.f) t->shape.scale = 1.0f / std::sqrt(static_cast<float>(shape->head_dim));
+  int64_t need = 0;
+  for (int32_t i = 0; i < t->ix.N; ++i) need = std::max(need, t->ix.kv_offset[i] + t->ix.kv_len[i]);
+  t->pool_tokens = shape->pool_tokens > 0 ? shape->pool_tokens : need;
+  if (need > t->pool_tokens) {
+    delete t;
+    set_error("a node lies outside the K/V pools (pool_tokens too small)");
+    return PST_E_INVALID_TREE;
+  }
+  if (t->shape.kv_stride_token == 0) t->shape.kv_stride_token = shape->head_dim;
+  if (t->shape.kv_stride_head == 0) t->shape.kv_stride_head = t->pool_tokens * shape->head_dim;
+  if (t->shape.kv_stride_token < shape->head_dim) {
+    delete t;
+    set_error("kv_stride_token smaller than head_dim");
+    return PST_E_INVALID_ARG;
+  }
+  const int eb = elem_bytes(shape->in_dtype);
+  if ((t->shape.kv_stride_token * eb) % 16 != 0 || (t->shape.kv_stride_head * eb) % 16 != 0) {
+    delete t;
+    set_error("K/V strides must be multiples of 16 bytes (128-bit loads)");
+    return PST_E_INVALID_ARG;
+  }
+  if (!(flags & PST_TREE_HOST_ONLY)) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipGetDevice(&t->device);
+    if (e != hipSuccess) {
+      delete t;
+      set_error(std::string("no HIP device: ") + hipGetErrorString(e));
+      return PST_E_NO_DEVICE;
+    }
+    const TreeIndex& ix = t->ix;
+    st = dev_upload(&t->d_node_off, ix.kv_offset.data(), ix.N, s);
+    if (st == PST_OK) st = dev_upload(&t->d_node_len, ix.kv_len.data(), ix.N, s);
+    if (st == PST_OK) st = dev_upload(&t->d_node_masked, ix.masked.data(), ix.N, s);
+    if (st == PST_OK) st = dev_upload(&t->d_nq_ptr, ix.nq_ptr.data(), ix.nq_ptr.size(), s);
+    if (st == PST_OK) st = dev_upload(&t->d_nq_idx, ix.nq_idx.data(), ix.nq_idx.size(), s);
+    if (st == PST_OK) st = dev_upload(&t->d_nq_mask, ix.nq_mask.data(), ix.nq_mask.size(), s);
+    if (st == PST_OK) {
+      e = hipStreamSynchronize(s);
+      if (e != hipSuccess) st = hip_fail("hipStreamSynchronize", e);
+    }
+    if (st != PST_OK) {
+      free_tree_device(t);
+      delete t;
+      return st;
+    }
+    t->on_device = true;
+  }
+  static uint64_t counter = 0;
+  t->generation = ++counter;
+  *out = t;
+  return PST_OK;
+}
+
+pst_status pst_tree_set_lengths(pst_tree_t t, const int32_t* kv_len, void* stream) {
+  if (!t || t->magic != kTreeMagic || !kv_len) {
+    set_error("bad tree or kv_len");
+    return PST_E_INVALID_ARG;
+  }
+  TreeIndex& ix = t->ix;
+  for (int32_t i = 0; i < ix.N; ++i) {
+    if (kv_len[i] < ix.kv_len[i]) {
+      set_error("kv_len may only grow (node " + std::to_string(i) + ")");
+      return PST_E_INVALID_ARG;
+    }
+    if (ix.masked[i] && kv_len[i] > 64) {
+      set_error("masked node " + std::to_string(i) + " would exceed 64 tokens");
+      return PST_E_INVALID_TREE;
+    }
+    if (ix.kv_offset[i] + kv_len[i] > t->pool_tokens) {
+      set_error("node " + std::to_string(i) + " would leave the K/V pools");
+      return PST_E_INVALID_TREE;
+    }
+  }
+  // Visible counts: every node on a path grows, except that a query's own
+  // masked node keeps its mask bits.
+  for (int32_t r = 0; r < ix.B; ++r) {
+    const int32_t own = ix.query_node[r];
+    int64_t vis = 0;
+    for (int32_t e = ix.qn_ptr[r]; e < ix.qn_ptr[r + 1]; ++e) {
+      const int32_t n = ix.qn_idx[e];
+      if (n == own && ix.masked[n] && ix.have_mask)
+        vis += __builtin_popcountll(ix.qmask[r]);
+      else
+        vis += kv_len[n];
+    }
+    ix.visible[r] = vis;
+  }
+  std::copy(kv_len, kv_len + ix.N, ix.kv_len.begin());
+  if (t->on_device && ix.N > 0) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(t->d_node_len, ix.kv_len.data(), ix.N * sizeof(int32_t), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail("hipMemcpyAsync", e);
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail("hipStreamSynchronize", e);
+  }
+  return PST_OK;
+}
+
+pst_status pst_tree_get_index(pst_tree_t t, pst_index_view* v) {
+  if (!t || t->magic != kTreeMagic || !v) {
+    set_error("bad tree or view");
+    return PST_E_INVALID_ARG;
+  }
+  const TreeIndex& ix = t->ix;
+  v->num_nodes = ix.N;
+  v->num_queries = ix.B;
+  v->num_entries = static_cast<int64_t>(ix.qn_idx.size());
+  v->depth = ix.depth.data();
+  v->n_q = ix.n_q.data();
+  v->qn_ptr = ix.qn_ptr.data();
+  v->qn_idx = ix.qn_idx.data();
+  v->nq_ptr = ix.nq_ptr.data();
+  v->nq_idx = ix.nq_idx.data();
+  v->nq_mask = ix.nq_mask.data();
+  v->visible = ix.visible.data();
+  return PST_OK;
+}
+
+pst_status pst_cost_model_create(int32_t n_rows, const int32_t* rows_grid, int32_t n_len, const int32_t* len_grid,
+                                 const int64_t* table, pst_cost_model_t* out) {
+  if (!out) {
+    set_error("out is NULL");
+    return PST_E_INVALID_ARG;
+  }
+  *out = nullptr;
+  if (n_rows < 1 || n_len < 2 || !rows_grid || !len_grid || !table) {
+    set_error("cost table needs >= 1 rows point, >= 2 length points and non-NULL arrays");
+    return PST_E_INVALID_ARG;
+  }
+  for (int i = 0; i < n_rows; ++i)
+    if (rows_grid[i] < 1 || (i && rows_grid[i] <= rows_grid[i - 1])) {
+      set_error("rows grid must be ascending and >= 1");
+      return PST_E_INVALID_ARG;
+    }
+  for (int j = 0; j < n_len; ++j)
+    if (len_grid[j] < 1 || (j && len_grid[j] <= len_grid[j - 1])) {
+      set_error("length grid must be ascending and >= 1");
+      return PST_E_INVALID_ARG;
+    }
+  for (int i = 0; i < n_rows; ++i)
+    for (int j = 0; j < n_len; ++j) {
+      const int64_t c = table[i * n_len + j];
+      if (c < 1 || (j && c < table[i * n_len + j - 1]) || (i && c < table[(i - 1) * n_len + j])) {
+        set_error("cost table must be >= 1 and non-decreasing along both axes");
+        return PST_E_INVALID_ARG;
+      }
+    }
+  pst_cost_s* c = new (std::nothrow) pst_cost_s();
+  if (!c) {
+    set_error("host allocation failed");
+    return PST_E_OOM;
+  }
+  c->model.rows_grid.assign(rows_grid, rows_grid + n_rows);
+  c->model.len_grid.assign(len_grid, len_grid + n_len);
+  c->model.table.assign(table, table + static_cast<size_t>(n_rows) * n_len);
+  *out = c;
+  return PST_OK;
+}
+
+pst_status pst_cost_model_lookup(pst_cost_model_t c, int32_t rows, int64_t len, int64_t* ns) {
+  if (!c || c->magic != kCostMagic || !ns) {
+    set_error("bad cost model or output");
+    return PST_E_INVALID_ARG;
+  }
+  *ns = c->model.lookup(rows, len);
+  return PST_OK;
+}
+
+pst_status pst_device_info(int32_t* num_cu, int32_t* per_cu) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error(std::string("no HIP device: ") + hipGetErrorString(e));
+    return PST_E_NO_DEVICE;
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail("hipDeviceGetAttribute", e);
+  int blocks = 0;
+  int he = pac_blocks_per_cu(PST_BF16, 128, &blocks);
+  if (he != 0) return hip_fail("occupancy query", static_cast<hipError_t>(he));
+  if (num_cu) *num_cu = cus;
+  if (per_cu) *per_cu = std::max(1, blocks);
+  return PST_OK;
+}
+
+pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* opts, void* stream, pst_plan_t* out) {
+  if (!out) {
+    set_error("out is NULL");
+    return PST_E_INVALID_ARG;
+  }
+  *out = nullptr;
+  if (!t || t->magic != kTreeMagic) {
+    set_error("bad tree");
+    return PST_E_INVALID_ARG;
+  }
+  if (cost && cost->magic != kCostMagic) {
+    set_error("bad cost model");
+    return PST_E_INVALID_ARG;
+  }
+  pst_plan_opts o{};
+  if (opts) o = *opts;
+  const bool host_only = (o.flags & PST_PLAN_HOST_ONLY) || !t->on_device;
+  const int32_t g = t->shape.num_q_heads / t->shape.num_kv_heads;
+  PlanOptions po;
+  po.tile = o.tile > 0 ? o.tile : kTile;
+  po.grid_steps = o.grid_steps > 0 ? o.grid_steps : 8;
+  po.fixed_chunk = o.fixed_chunk;
+  po.no_split = (o.flags & PST_PLAN_NO_SPLIT) != 0;
+  po.query_guided = (o.flags & PST_PLAN_QUERY_GUIDED) != 0;
+  const int32_t default_rows = t->shape.in_dtype == PST_F32 ? kMaxRowsDot : kMaxRows;
+  po.r_max = o.max_rows > 0 ? o.max_rows : default_rows;
+  if (po.tile % kTile != 0 || po.r_max > kMaxRows || po.fixed_chunk < 0 || po.fixed_chunk % kTile != 0 ||
+      o.num_bins < 0) {
+    set_error("tile and fixed_chunk must be multiples of 64, max_rows <= 256, num_bins >= 0");
+    return PST_E_INVALID_ARG;
+  }
+  if (t->shape.in_dtype == PST_F32 && (po.query_guided ? g : po.r_max) > kMaxRowsDot) {
+    set_error("float32 inputs run on the dot-product path: rows per workgroup must be <= 16");
+    return PST_E_UNSUPPORTED;
+  }
+  if (po.query_guided && g > kMaxRows) {
+    set_error("GQA group exceeds the rows of one workgroup");
+    return PST_E_UNSUPPORTED;
+  }
+  if (o.num_bins > 0) {
+    po.m = o.num_bins;
+  } else if (!host_only) {
+    int32_t cus = 0, per = 0;
+    pst_status st = pst_device_info(&cus, &per);
+    if (st != PST_OK) return st;
+    po.m = std::max(1, cus * per / t->shape.num_kv_heads);
+  } else {
+    po.m = std::max(1, 256 / t->shape.num_kv_heads);
+  }
+  CostModel fallback;
+  const CostModel* cm = nullptr;
+  if (cost) {
+    cm = &cost->model;
+  } else {
+    fallback = analytic_cost_model(g, t->shape.head_dim, elem_bytes(t->shape.in_dtype));
+    cm = &fallback;
+  }
+  pst_plan_s* p = new (std::nothrow) pst_plan_s();
+  if (!p) {
+    set_error("host allocation failed");
+    return PST_E_OOM;
+  }
+  p->tree = t;
+  p->generation = t->generation;
+  p->opts = po;
+  pst_status st = build_plan(t->ix, g, *cm, po, &p->r);
+  if (st != PST_OK) {
+    delete p;
+    return st;
+  }
+  if (!p->r.slot_ptr.empty() && p->r.slot_ptr.back() > INT32_MAX / 2) {
+    delete p;
+    set_error("too many partial slots");
+    return PST_E_UNSUPPORTED;
+  }
+  if (!host_only) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::vector<int32_t> es32(p->r.entry_slot.begin(), p->r.entry_slot.end());
+    st = dev_upload(&p->d_tasks, p->r.tasks.data(), p->r.tasks.size(), s);
+    if (st == PST_OK) st = dev_upload(&p->d_bin_ptr, p->r.bin_ptr.data(), p->r.bin_ptr.size(), s);
+    if (st == PST_OK) st = dev_upload(&p->d_entry_slot, es32.data(), es32.size(), s);
+    if (st == PST_OK) st = dev_upload(&p->d_slot_ptr, p->r.slot_ptr.data(), p->r.slot_ptr.size(), s);
+    if (st == PST_OK) {
+      hipError_t e = hipStreamSynchronize(s);
+      if (e != hipSuccess) st = hip_fail("hipStreamSynchronize", e);
+    }
+    if (st != PST_OK) {
+      free_plan_device(p);
+      delete p;
+      return st;
+    }
+    p->on_device = true;
+  }
+  t->live_plans++;
+  *out = p;
+  return PST_OK;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+static void workspace_layout(const pst_plan_s* p, size_t* o_bytes, size_t* total) {
+  const pst_shape& s = p->tree->shape;
+  const size_t slots = p->r.slot_ptr.empty() ? 0 : static_cast<size_t>(p->r.slot_ptr.back());
+  *o_bytes = align256(slots * s.num_q_heads * s.head_dim * sizeof(float));
+  *total = *o_bytes + align256(slots * s.num_q_heads * sizeof(float));
+}
+
+pst_status pst_plan_workspace_size(pst_plan_t p, size_t* bytes) {
+  if (!p || p->magic != kPlanMagic || !bytes) {
+    set_error("bad plan or output");
+    return PST_E_INVALID_ARG;
+  }
+  size_t ob = 0;
+  workspace_layout(p, &ob, bytes);
+  return PST_OK;
+}
+
+pst_status pst_plan_get(pst_plan_t p, pst_plan_view* v) {
+  if (!p || p->magic != kPlanMagic || !v) {
+    set_error("bad plan or view");
+    return PST_E_INVALID_ARG;
+  }
+  v->num_bins = p->opts.m;
+  v->num_tasks = static_cast<int32_t>(p->r.tasks.size());
+  v->num_queries = p->tree->ix.B;
+  v->num_nodes = p->tree->ix.N;
+  v->num_slots = p->r.slot_ptr.empty() ? 0 : p->r.slot_ptr.back();
+  v->num_entries = static_cast<int64_t>(p->r.entry_slot.size());
+  v->tasks = reinterpret_cast<const int32_t*>(p->r.tasks.data());
+  v->bin_ptr = p->r.bin_ptr.data();
+  v->slot_ptr = p->r.slot_ptr.data();
+  v->entry_slot = p->r.entry_slot.data();
+  v->piece_len = p->r.piece_len.data();
+  v->b_eff = p->r.b_eff.data();
+  v->rows_per_group = p->r.rows_per_group.data();
+  v->bin_load = p->r.bin_load.data();
+  v->makespan = p->r.makespan;
+  v->cost_l = p->r.cost_l;
+  v->chosen_k = p->r.chosen_k;
+  v->max_rows = p->opts.query_guided ? p->tree->shape.num_q_heads / p->tree->shape.num_kv_heads : p->opts.r_max;
+  return PST_OK;
+}
+
+static pst_status check_run(pst_plan_t p, const void* ws, size_t ws_bytes) {
+  if (!p || p->magic != kPlanMagic) {
+    set_error("bad plan");
+    return PST_E_INVALID_ARG;
+  }
+  if (!p->on_device || !p->tree->on_device) {
+    set_error("plan or tree was built host-only");
+    return PST_E_NO_DEVICE;
+  }
+  if (p->generation != p->tree->generation) {
+    set_error("plan is stale: its tree changed");
+    return PST_E_PLAN_STALE;
+  }
+  size_t ob = 0, need = 0;
+  workspace_layout(p, &ob, &need);
+  if (need > 0 && (!ws || ws_bytes < need)) {
+    set_error("workspace missing or smaller than pst_plan_workspace_size");
+    return PST_E_WORKSPACE;
+  }
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) {
+    set_error("workspace must be 256-byte aligned");
+    return PST_E_WORKSPACE;
+  }
+  return PST_OK;
+}
+
+pst_status pst_pac(pst_plan_t p, const void* q, const void* k, const void* v, void* ws, size_t ws_bytes,
+                   void* stream) {
+  pst_status st = check_run(p, ws, ws_bytes);
+  if (st != PST_OK) return st;
+  if (p->r.tasks.empty()) return PST_OK;
+  if (!q || !k || !v) {
+    set_error("q, k_pool or v_pool is NULL");
+    return PST_E_INVALID_ARG;
+  }
+  const pst_tree_s* t = p->tree;
+  size_t ob = 0, total = 0;
+  workspace_layout(p, &ob, &total);
+  PacParams pp{};
+  pp.q = q;
+  pp.k = k;
+  pp.v = v;
+  pp.opart = static_cast<float*>(ws);
+  pp.lsepart = reinterpret_cast<float*>(static_cast<char*>(ws) + ob);
+  pp.tasks = p->d_tasks;
+  pp.bin_ptr = p->d_bin_ptr;
+  pp.node_off = t->d_node_off;
+  pp.node_len = t->d_node_len;
+  pp.nq_ptr = t->d_nq_ptr;
+  pp.nq_idx = t->d_nq_idx;
+  pp.nq_mask = t->d_nq_mask;
+  pp.entry_slot = p->d_entry_slot;
+  pp.node_masked = t->d_node_masked;
+  pp.stride_head = t->shape.kv_stride_head;
+  pp.stride_token = t->shape.kv_stride_token;
+  pp.num_bins = p->opts.m;
+  pp.hq = t->shape.num_q_heads;
+  pp.hkv = t->shape.num_kv_heads;
+  pp.g = pp.hq / pp.hkv;
+  pp.scale_log2 = t->shape.scale * 1.4426950408889634f;
+  int e = launch_pac(pp, t->shape.in_dtype, t->shape.head_dim, stream);
+  if (e != 0) return hip_fail("PAC launch", static_cast<hipError_t>(e));
+  return PST_OK;
+}
+
+pst_status pst_por(pst_plan_t p, void* out, float* lse_out, const void* ws, size_t ws_bytes, void* stream) {
+  pst_status st = check_run(p, ws, ws_bytes);
+  if (st != PST_OK) return st;
+  const pst_tree_s* t = p->tree;
+  if (t->ix.B == 0) return PST_OK;
+  if (!out) {
+    set_error("out is NULL");
+    return PST_E_INVALID_ARG;
+  }
+  size_t ob = 0, total = 0;
+  workspace_layout(p, &ob, &total);
+  PorParams pp{};
+  pp.opart = static_cast<const float*>(ws);
+  pp.lsepart = reinterpret_cast<const float*>(static_cast<const char*>(ws) + ob);
+  pp.slot_ptr = p->d_slot_ptr;
+  pp.out = out;
+  pp.lse_out = lse_out;
+  pp.num_queries = t->ix.B;
+  pp.hq = t->shape.num_q_heads;
+  int e = launch_por(pp, t->shape.head_dim, t->shape.out_dtype, stream);
+  if (e != 0) return hip_fail("POR launch", static_cast<hipError_t>(e));
+  return PST_OK;
+}
+
+pst_status pst_decode_attn(pst_plan_t p, const void* q, const void* k, const void* v, void* out, float* lse_out,
+                           void* ws, size_t ws_bytes, void* stream) {
+  pst_status st = pst_pac(p, q, k, v, ws, ws_bytes, stream);
+  if (st != PST_OK) return st;
+  return pst_por(p, out, lse_out, ws, ws_bytes, stream);
+}
+
+pst_status pst_free(void* obj) {
+  if (!obj) return PST_OK;
+  const uint32_t magic = *static_cast<uint32_t*>(obj);
+  if (magic == kTreeMagic) {
+    pst_tree_s* t = static_cast<pst_tree_s*>(obj);
+    if (t->live_plans > 0) {
+      set_error("tree still has live plans: free them first");
+      return PST_E_INVALID_ARG;
+    }
+    free_tree_device(t);
+    t->magic = 0;
+    delete t;
+    return PST_OK;
+  }
+  if (magic == kPlanMagic) {
+    pst_plan_s* p = static_cast<pst_plan_s*>(obj);
+    if (p->tree) p->tree->live_plans--;
+    free_plan_device(p);
+    p->magic = 0;
+    delete p;
+    return PST_OK;
+  }
+  if (magic == kCostMagic) {
+    pst_cost_s* c = static_cast<pst_cost_s*>(obj);
+    c->magic = 0;
+    delete c;
+    return PST_OK;
+  }
+  set_error("pst_free: not a pst object");
+  return PST_E_INVALID_ARG;
+}
+
+pst_status pst_bench_flush(void* buf, size_t bytes, void* stream) {
+  if (!buf || bytes % 16 != 0) {
+    set_error("flush buffer NULL or size not a multiple of 16");
+    return PST_E_INVALID_ARG;
+  }
+  int e = launch_flush(buf, bytes, stream);
+  if (e != 0) return hip_fail("flush launch", static_cast<hipError_t>(e));
+  return PST_OK;
+}
+
+pst_status pst_bench_read(const void* buf, size_t bytes, float* sink, void* stream) {
+  if (!buf || !sink || bytes % 16 != 0) {
+    set_error("read buffer or sink NULL, or size not a multiple of 16");
+    return PST_E_INVALID_ARG;
+  }
+  int e = launch_read(buf, bytes, sink, stream);
+  if (e != 0) return hip_fail("read launch", static_cast<hipError_t>(e));
+  return PST_OK;
+}
+
+}  // extern "C"

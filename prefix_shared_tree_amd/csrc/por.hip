@@ -1,0 +1,131 @@
+// Partial output reduction (POR) and measurement helpers, gfx950.
+//
+// CoDec: Prefix-Shared Decoding Kernel for LLMs, section 块内内核原语 (POR
+// kernel): two partial results of the same query are merged at the common
+// maximum m = max(m1, m2) with weights s_i e^{m_i - m}; section 块间启动与树归约:
+// the merge is associative and commutative, so the tree reduction becomes one
+// independent chain per query, and the chains run in parallel.  With
+// normalised partials and their natural-log LSE (DEFT: Decoding with Flash
+// Tree-Attention, section 速读 and A.4 phase 2; FlashDecoding's second level
+// in the KV-cache engineering blog, section 4) the n-way merge of a chain is
+//     L* = max_i LSE_i,  w_i = exp(LSE_i - L*),
+//     O = sum_i w_i O_i / sum_i w_i,  LSE = L* + ln sum_i w_i,
+// which is the binary POR folded over the chain; empty partials (LSE = -inf)
+// get weight 0.  One workgroup per query; threads own (q-head, 4 channels).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pst_internal.h"
+
+namespace pst {
+namespace {
+
+typedef __bf16 bf16x2n __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPorThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+template <int D, bool BF16_OUT>
+__global__ __launch_bounds__(kPorThreads) void por_kernel(PorParams p) {
+  const int r = blockIdx.x;
+  const int64_t s0 = p.slot_ptr[r], s1 = p.slot_ptr[r + 1];
+  constexpr int C4 = D / 4;
+  for (int idx = threadIdx.x; idx < p.hq * C4; idx += kPorThreads) {
+    const int h = idx / C4, c4 = idx % C4;
+    float lmax = kNegInf;
+    for (int64_t s = s0; s < s1; ++s) lmax = fmaxf(lmax, p.lsepart[s * p.hq + h]);
+    const float lref = lmax == kNegInf ? 0.f : lmax;
+    float z = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t s = s0; s < s1; ++s) {
+      const float wgt = __builtin_amdgcn_exp2f((p.lsepart[s * p.hq + h] - lref) * kLog2e);
+      if (wgt == 0.f) continue;  // empty partial: its O may be anything
+      const float4 x = *reinterpret_cast<const float4*>(p.opart + (s * p.hq + h) * D + c4 * 4);
+      z += wgt;
+      acc.x += wgt * x.x;
+      acc.y += wgt * x.y;
+      acc.z += wgt * x.z;
+      acc.w += wgt * x.w;
+    }
+    const float inv = z > 0.f ? 1.f / z : 0.f;
+    const int64_t o = (static_cast<int64_t>(r) * p.hq + h) * D + c4 * 4;
+    if (BF16_OUT) {
+      f32x2 a = {acc.x * inv, acc.y * inv}, b = {acc.z * inv, acc.w * inv};
+      uint2 u;
+      u.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2n));
+      u.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2n));
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = u;
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) =
+          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    if (p.lse_out && c4 == 0) p.lse_out[static_cast<int64_t>(r) * p.hq + h] = z > 0.f ? lref + __logf(z) : kNegInf;
+  }
+}
+
+// Overwrite a buffer with 128-bit stores (evicts L2 and the last-level cache).
+__global__ __launch_bounds__(256) void flush_kernel(uint4* buf, size_t n16) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+    buf[i] = make_uint4(static_cast<uint32_t>(i), 0u, 0u, 0u);
+}
+
+// Stream a buffer with 128-bit loads; one float per workgroup keeps the loads alive.
+__global__ __launch_bounds__(256) void read_kernel(const uint4* buf, size_t n16, float* sink) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  uint32_t acc = 0;
+  size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride], d = buf[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = buf[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t x = 0;
+    for (int j = 0; j < 256; ++j) x ^= red[j];
+    sink[blockIdx.x] = static_cast<float>(x & 1u);
+  }
+}
+
+}  // namespace
+
+int launch_por(const PorParams& p, int head_dim, int out_dtype, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(p.num_queries), block(kPorThreads);
+  const bool bf = out_dtype == PST_BF16;
+  if (head_dim == 128) {
+    if (bf)
+      hipLaunchKernelGGL((por_kernel<128, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((por_kernel<128, false>), grid, block, 0, s, p);
+  } else {
+    if (bf)
+      hipLaunchKernelGGL((por_kernel<64, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((por_kernel<64, false>), grid, block, 0, s, p);
+  }
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_flush(void* buf, size_t bytes, void* stream) {
+  hipLaunchKernelGGL(flush_kernel, dim3(4096), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint4*>(buf), bytes / 16);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_read(const void* buf, size_t bytes, float* sink, void* stream) {
+  hipLaunchKernelGGL(read_kernel, dim3(4096), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(buf), bytes / 16, sink);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace pst

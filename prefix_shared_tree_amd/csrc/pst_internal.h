@@ -1,0 +1,129 @@
+// Internal declarations of libpst: host objects, the plan builder and the
+// kernel parameter blocks shared between the host library and the kernels.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "pst.h"
+
+namespace pst {
+
+constexpr uint32_t kTreeMagic = 0x31545350u;  // "PST1"
+constexpr uint32_t kPlanMagic = 0x32545350u;  // "PST2"
+constexpr uint32_t kCostMagic = 0x33545350u;  // "PST3"
+
+constexpr int kTile = 64;         // tokens per K/V tile of the partial-attention kernel
+constexpr int kMaxRows = 256;     // rows one workgroup holds (MFMA path: 8 waves x 32 rows)
+constexpr int kMfmaMinRows = 16;  // rows from which a bf16 piece uses the matrix cores
+constexpr int kMaxRowsDot = 16;   // the dot-product path keeps up to this many rows in registers
+constexpr int kPacThreads = 512;  // 8 wavefronts of 64
+
+void set_error(const std::string& msg);
+
+// Piece of partial attention: one node, one KV range, one row group.  Rows
+// of node i are (node->query entry e, head j in the GQA group) = e * g + j.
+struct Task {
+  int32_t node;
+  int32_t piece;
+  int32_t kv_begin;
+  int32_t kv_len;
+  int32_t row_begin;
+  int32_t row_count;
+  int32_t flags;  // PST_TASK_LAST_PIECE
+  int32_t reserved;
+};
+static_assert(sizeof(Task) == 32, "task layout");
+
+struct CostModel {
+  uint32_t magic = kCostMagic;
+  std::vector<int32_t> rows_grid;
+  std::vector<int32_t> len_grid;
+  std::vector<int64_t> table;  // [rows][len]
+  int64_t lookup(int64_t rows, int64_t len) const;
+};
+
+// Validates and indexes a tree on the host.  Returns PST_OK or an error with set_error().
+struct TreeIndex {
+  int32_t N = 0, B = 0;
+  bool have_mask = false;
+  std::vector<int32_t> parent, kv_len, query_node;
+  std::vector<int64_t> kv_offset;
+  std::vector<uint8_t> masked;
+  std::vector<uint64_t> qmask;
+  std::vector<int32_t> depth, n_q, qn_ptr, qn_idx, nq_ptr, nq_idx;
+  std::vector<uint64_t> nq_mask;
+  std::vector<int64_t> visible;
+};
+pst_status build_tree_index(const pst_tree_desc& d, TreeIndex* out);
+
+struct PlanOptions {
+  int32_t m = 1;
+  int32_t r_max = kMaxRows;
+  int32_t tile = kTile;
+  int32_t grid_steps = 8;
+  int32_t fixed_chunk = 0;
+  bool no_split = false;
+  bool query_guided = false;
+};
+
+struct PlanResult {
+  std::vector<Task> tasks;
+  std::vector<int32_t> bin_ptr;
+  std::vector<int64_t> slot_ptr, entry_slot;
+  std::vector<int32_t> piece_len, b_eff, rows_per_group;
+  std::vector<int64_t> bin_load;
+  int64_t makespan = 0, cost_l = 0;
+  int32_t chosen_k = 0;
+};
+pst_status build_plan(const TreeIndex& ix, int32_t g, const CostModel& cost, const PlanOptions& o,
+                      PlanResult* out);
+CostModel analytic_cost_model(int32_t g, int32_t head_dim, int32_t elem_bytes);
+
+// ---------------------------------------------------------------------------
+// Kernel parameter blocks (passed by value)
+// ---------------------------------------------------------------------------
+struct PacParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* opart;    // [slots][hq][d]
+  float* lsepart;  // [slots][hq]
+  const Task* tasks;
+  const int32_t* bin_ptr;
+  const int64_t* node_off;
+  const int32_t* node_len;
+  const int32_t* nq_ptr;
+  const int32_t* nq_idx;
+  const uint64_t* nq_mask;
+  const int32_t* entry_slot;
+  const uint8_t* node_masked;
+  int64_t stride_head;   // elements
+  int64_t stride_token;  // elements
+  int32_t num_bins;
+  int32_t hq;
+  int32_t hkv;
+  int32_t g;
+  float scale_log2;  // scale * log2(e)
+};
+
+struct PorParams {
+  const float* opart;
+  const float* lsepart;
+  const int64_t* slot_ptr;
+  void* out;
+  float* lse_out;
+  int32_t num_queries;
+  int32_t hq;
+};
+
+// Kernel launchers (defined in the .hip sources).  Return hipError_t as int.
+int launch_pac(const PacParams& p, int in_dtype, int head_dim, void* stream);
+int launch_por(const PorParams& p, int head_dim, int out_dtype, void* stream);
+int launch_flush(void* buf, size_t bytes, void* stream);
+int launch_read(const void* buf, size_t bytes, float* sink, void* stream);
+int pac_blocks_per_cu(int in_dtype, int head_dim, int* blocks);
+size_t pac_lds_bytes();
+
+}  // namespace pst

@@ -1,0 +1,225 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances (max-abs, float32 outputs): 1e-5 for float32 inputs, 2e-3 for
+bfloat16 inputs with float32 accumulation.  bfloat16 outputs are checked to
+be the round-to-nearest-even of an output within that tolerance (within one
+bf16 ulp of the oracle plus 2e-3).  Full-size workloads are checked on
+sampled queries (every head of each sampled query).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import prefix_shared_tree_amd as pst  # noqa: E402
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run(spec, *, out_dtype="f32", q_scale=1.0, tensors=None, **plan_kw):
+    q, k, v = tensors if tensors is not None else workloads.make_tensors(spec, "cuda", q_scale=q_scale)
+    tree = pst.Tree.from_spec(spec, out_dtype=out_dtype)
+    plan = pst.Plan(tree, **plan_kw)
+    out, lse = pst.decode_attn(plan, q, k, v)
+    torch.cuda.synchronize()
+    return (q, k, v), plan, out, lse
+
+
+def check(spec, tensors, out, lse, queries=None, tol=None):
+    q, k, v = tensors
+    if queries is None:
+        queries = list(range(spec.num_queries))
+    O, L = oracle.attend(spec, q, k, v, queries=queries)
+    got = out[queries].double().cpu().numpy()
+    tol = TOL[spec.dtype] if tol is None else tol
+    err = np.abs(got - O).max() if len(queries) else 0.0
+    lerr = np.abs(lse[queries].double().cpu().numpy() - L).max() if len(queries) else 0.0
+    say(f"  {spec.name}: max|dO| = {err:.3e}, max|dLSE| = {lerr:.3e} over {len(queries)} queries")
+    assert err <= tol, err
+    assert lerr <= max(tol, 1e-5) * 4, lerr
+    return err
+
+
+def sample(n, k, seed=0):
+    if n <= k:
+        return list(range(n))
+    rng = np.random.default_rng(seed)
+    return sorted(rng.choice(n, size=k, replace=False).tolist())
+
+
+@pytest.mark.parametrize("name", ["1", "3"])
+def test_config_full(name):
+    spec = workloads.config(name)
+    say(f"config {name}: {spec.name}")
+    t, plan, out, lse = run(spec)
+    check(spec, t, out, lse)
+
+
+def test_config2_sampled():
+    spec = workloads.config("2")
+    say(f"config 2: {spec.name}")
+    t, plan, out, lse = run(spec)
+    check(spec, t, out, lse, queries=sample(64, 12))
+
+
+def test_config4_sampled():
+    spec = workloads.config("4")
+    say(f"config 4: {spec.name}")
+    t, plan, out, lse = run(spec)
+    check(spec, t, out, lse, queries=sample(spec.num_queries, 48, 1))
+
+
+def test_config5_mqa_sampled():
+    spec = workloads.config("5-mqa")
+    say(f"config 5-mqa: {spec.name}")
+    t, plan, out, lse = run(spec)
+    check(spec, t, out, lse, queries=sample(spec.num_queries, 24, 2))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_trees(seed):
+    """Random forests spanning the dot-product / matrix-core switch (rows 1..300)."""
+    rng = np.random.default_rng(seed)
+    dtype = "f32" if seed % 4 == 0 else "bf16"
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 4, 8, 32]))
+    d = 64 if seed % 5 == 0 else 128
+    spec = workloads.random_tree(1000 + seed, max_nodes=8, max_len=int(rng.choice([40, 300, 2000])),
+                                 max_queries=int(rng.choice([3, 12, 40])), num_q_heads=hkv * g, num_kv_heads=hkv,
+                                 head_dim=d, dtype=dtype, masked_prob=0.3 if seed % 3 == 0 else 0.0)
+    if dtype == "f32" and g > 16:
+        spec = workloads.random_tree(1000 + seed, max_nodes=8, max_len=300, max_queries=12, num_q_heads=hkv * 4,
+                                     num_kv_heads=hkv, head_dim=d, dtype=dtype)
+    say(f"random tree seed {seed}: dtype {spec.dtype} H {spec.num_q_heads}/{spec.num_kv_heads} d {spec.head_dim} "
+        f"N {spec.num_nodes} B {spec.num_queries}")
+    t, plan, out, lse = run(spec, num_bins=int(rng.choice([0, 3, 17])))
+    check(spec, t, out, lse)
+
+
+@pytest.mark.parametrize("rows", [1, 2, 4, 8, 12, 15, 16, 17, 31, 32, 48, 64, 65, 100, 128, 129, 200, 256])
+def test_row_counts_single_node(rows):
+    """One node shared by `rows` MQA rows (g = rows, one query): every row bucket and a ragged tail."""
+    spec = workloads.TreeSpec(f"rows{rows}", np.array([-1]), np.array([1000]), np.array([0]), np.array([0]),
+                              rows, 1, 128, "bf16", 77)
+    say(f"rows {rows}")
+    t, plan, out, lse = run(spec, num_bins=5)
+    check(spec, t, out, lse)
+
+
+def test_max_rows_split():
+    """More rows than one workgroup holds: the planner cuts row groups (> 256 rows)."""
+    lens = [700] + [3] * 20
+    spec = workloads.TreeSpec("rowgroups", np.array([-1] + [0] * 20), np.array(lens),
+                              np.concatenate([[0], np.cumsum(lens)[:-1]]), np.arange(1, 21), 32, 1, 128, "bf16", 8)
+    t, plan, out, lse = run(spec, num_bins=9)
+    assert plan.view()["rows_per_group"][0] < 20 * 32
+    check(spec, t, out, lse)
+
+
+def test_bf16_output_rounding():
+    spec = workloads.config("3")
+    t, plan, out_bf, _ = run(spec, out_dtype="bf16")
+    _, _, out32, lse32 = run(spec, tensors=t)
+    assert out_bf.dtype == torch.bfloat16
+    # POR rounds its float32 result to nearest even: identical to rounding the float32 output.
+    assert torch.equal(out_bf, out32.to(torch.bfloat16))
+
+
+def test_query_guided_baseline():
+    spec = workloads.config("3")
+    t, plan, out, lse = run(spec, query_guided=True)
+    v = plan.view()
+    assert (v["tasks"][:, 5] == spec.group).all()
+    check(spec, t, out, lse, queries=sample(128, 32, 3))
+
+
+@pytest.mark.parametrize("kw", [dict(no_split=True), dict(fixed_chunk=256), dict(num_bins=1)])
+def test_plan_variants(kw):
+    spec = workloads.config("3")
+    t, plan, out, lse = run(spec, **kw)
+    check(spec, t, out, lse, queries=sample(128, 16, 4))
+
+
+def test_deterministic():
+    spec = workloads.config("3")
+    t, plan, out1, lse1 = run(spec)
+    out2, lse2 = pst.decode_attn(plan, *t)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_plan_reuse_after_growth():
+    spec = workloads.config("3")
+    q, k, v = workloads.make_tensors(spec, "cuda", kv_tokens=spec.total_tokens + 64)
+    tree = pst.Tree.from_spec(spec, out_dtype="f32", pool_tokens=spec.total_tokens + 64)
+    plan = pst.Plan(tree)
+    lens = spec.kv_len.copy()
+    lens[-1] += 50  # the last leaf is the last run of the pool: it can grow in place
+    tree.set_lengths(lens)
+    out, lse = pst.decode_attn(plan, q, k, v)
+    torch.cuda.synchronize()
+    grown = workloads.TreeSpec("grown", spec.parent, lens, spec.kv_offset, spec.query_node, 32, 8, 128, "bf16", 3)
+    check(grown, (q, k, v), out, lse, queries=[0, 126, 127])
+
+
+def test_peaked_attention_reported():
+    """Queries scaled by 8 make attention peaked; reported against the bf16 tolerance."""
+    spec = workloads.config("3")
+    t, plan, out, lse = run(spec, q_scale=8.0)
+    check(spec, t, out, lse, queries=sample(128, 16, 5), tol=2e-2)
+
+
+def test_empty_batch_and_single_token():
+    spec = workloads.TreeSpec("empty", np.array([-1]), np.array([5]), np.array([0]), np.zeros(0, dtype=np.int32),
+                              4, 4, 64, "f32", 1)
+    q = torch.zeros((0, 4, 64), device="cuda")
+    k = torch.randn((4, 5, 64), device="cuda")
+    tree = pst.Tree.from_spec(spec, out_dtype="f32")
+    plan = pst.Plan(tree)
+    out, lse = pst.decode_attn(plan, q, k, k)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 4, 64)
+    spec1 = workloads.TreeSpec("one", np.array([-1]), np.array([1]), np.array([0]), np.array([0, 0]), 8, 2, 128,
+                               "bf16", 2)
+    t, plan, out, lse = run(spec1)
+    check(spec1, t, out, lse)
+
+
+def test_token_major_strides():
+    """K/V pools in [T, H_kv, d] layout through the stride arguments."""
+    spec = workloads.config("3")
+    q, k, v = workloads.make_tensors(spec, "cuda")
+    kt = k.permute(1, 0, 2).contiguous()
+    vt = v.permute(1, 0, 2).contiguous()
+    tree = pst.Tree.from_spec(spec, out_dtype="f32", kv_stride_head=128, kv_stride_token=8 * 128)
+    plan = pst.Plan(tree)
+    out, lse = pst.decode_attn(plan, q, kt, vt)
+    torch.cuda.synchronize()
+    check(spec, (q, k, v), out, lse, queries=sample(128, 16, 6))
+
+
+def test_workspace_errors():
+    spec = workloads.config("1")
+    q, k, v = workloads.make_tensors(spec, "cuda")
+    tree = pst.Tree.from_spec(spec, out_dtype="f32")
+    plan = pst.Plan(tree)
+    small = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pst.PstError) as e:
+        pst.decode_attn(plan, q, k, v, ws=small)
+    assert e.value.code == "PST_E_WORKSPACE"

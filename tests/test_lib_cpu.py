@@ -1,0 +1,204 @@
+"""The C-ABI library on the host (no GPU): exports, bit-exact index and plan
+against the oracle, and every error path that can be forced from the host."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import prefix_shared_tree_amd as pst
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROWS = [1, 2, 4, 8, 16, 32, 64, 128, 256]
+LENS = [16 << i for i in range(13)]
+
+
+def test_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "pst.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"\b(pst_[a-z_]+)\s*\(", header))
+    assert declared, "no declarations found"
+    for name in sorted(declared):
+        assert hasattr(pst._lib, name), name
+    assert declared == set(pst.EXPORTS)
+
+
+def _tree(spec, **kw):
+    return pst.Tree.from_spec(spec, host_only=True, **kw)
+
+
+def _specs():
+    out = [workloads.random_tree(s, max_nodes=9, max_len=300, max_queries=10, num_q_heads=8, num_kv_heads=2,
+                                 masked_prob=0.4 if s % 3 == 0 else 0.0) for s in range(25)]
+    out += [workloads.config(n) for n in ("1", "2", "3", "4", "5-mqa")]
+    return out
+
+
+@pytest.mark.parametrize("spec", _specs(), ids=lambda s: s.name)
+def test_index_bit_exact(spec):
+    got = _tree(spec).index()
+    want = oracle.build_index(spec)
+    for key in want:
+        assert np.array_equal(got[key], want[key].astype(got[key].dtype)), key
+
+
+def _table(kind, seed=0):
+    if kind == "affine":
+        t = [[900 + 3 * r + 2 * L for L in LENS] for r in ROWS]
+    else:
+        rng = np.random.default_rng(seed)
+        t = (np.cumsum(np.cumsum(rng.integers(1, 60, size=(9, 13)), axis=0), axis=1) + 400).tolist()
+    return t
+
+
+PLAN_CASES = [
+    dict(m=32, r_max=256),
+    dict(m=7, r_max=16),
+    dict(m=1, r_max=256),
+    dict(m=64, r_max=8),
+    dict(m=16, query_guided=True),
+    dict(m=16, no_split=True),
+    dict(m=16, fixed_chunk=128),
+    dict(m=40, r_max=64, grid_steps=3),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PLAN_CASES)))
+@pytest.mark.parametrize("spec", _specs()[::3] + _specs()[-5:], ids=lambda s: s.name)
+@pytest.mark.parametrize("tkind", ["affine", "random"])
+def test_plan_bit_exact(spec, case, tkind):
+    c = dict(PLAN_CASES[case])
+    if spec.dtype == "f32" and not c.get("query_guided"):
+        c["r_max"] = min(c.get("r_max", 16), 16)
+    if spec.dtype == "f32" and c.get("query_guided") and spec.group > 16:
+        pytest.skip("f32 rows per workgroup capped at 16")
+    table = _table(tkind, seed=case)
+    cm = pst.CostModel(ROWS, LENS, table)
+    tree = _tree(spec)
+    plan = pst.Plan(tree, cm, num_bins=c["m"], max_rows=c.get("r_max", 0), grid_steps=c.get("grid_steps", 0),
+                    fixed_chunk=c.get("fixed_chunk", 0), query_guided=c.get("query_guided", False),
+                    no_split=c.get("no_split", False), host_only=True)
+    got = plan.view()
+    ix = oracle.build_index(spec)
+    want = oracle.plan(ix, spec.kv_len, spec.group, oracle.CostTable(ROWS, LENS, table), c["m"],
+                       r_max=c.get("r_max", 256), grid_steps=c.get("grid_steps", 8),
+                       query_guided=c.get("query_guided", False), no_split=c.get("no_split", False),
+                       fixed_chunk=c.get("fixed_chunk", 0))
+    assert np.array_equal(got["tasks"][:, :7], want["tasks"])
+    for key in ("bin_ptr", "slot_ptr", "entry_slot", "piece_len", "b_eff", "rows_per_group", "bin_load"):
+        assert np.array_equal(got[key], want[key].astype(got[key].dtype)), key
+    for key in ("makespan", "cost_l", "chosen_k", "num_slots"):
+        assert got[key] == want[key], key
+
+
+def test_cost_lookup_matches_oracle():
+    table = _table("random", seed=3)
+    cm = pst.CostModel(ROWS, LENS, table)
+    ot = oracle.CostTable(ROWS, LENS, table)
+    for rows in [1, 2, 3, 5, 16, 17, 200, 256, 300]:
+        for L in [1, 15, 16, 17, 63, 64, 65, 1000, 4000, 65535, 65536, 65537, 10 ** 6]:
+            assert cm.lookup(rows, L) == ot.lookup(rows, L)
+
+
+# ---------------------------------------------------------------------------
+# Error paths (forced from the host)
+# ---------------------------------------------------------------------------
+
+def _raises(code, fn, *a, **kw):
+    with pytest.raises(pst.PstError) as e:
+        fn(*a, **kw)
+    assert e.value.code == code, str(e.value)
+    return e.value
+
+
+BAD_TREES = {
+    "parent_after_child": dict(parent=[-1, 2, 0]),
+    "zero_length": dict(kv_len=[4, 0, 3]),
+    "negative_offset": dict(kv_offset=[0, -1, 9]),
+    "query_on_missing_node": dict(query_node=[1, 5]),
+    "masked_node_too_long": dict(kv_len=[4, 65, 3], node_masked=[0, 1, 0], query_mask=[1, 0]),
+    "mask_bit_past_length": dict(node_masked=[0, 1, 0], query_mask=[1 << 2, 0]),
+    "query_sees_nothing": dict(parent=[-1, -1, 0], node_masked=[0, 1, 0], query_mask=[0, 0]),
+    "node_outside_pool": dict(pool_tokens=8),
+}
+
+
+@pytest.mark.parametrize("case", sorted(BAD_TREES))
+def test_invalid_tree(case):
+    base = dict(parent=[-1, 0, 0], kv_len=[4, 2, 3], kv_offset=[0, 4, 6], query_node=[1, 2], node_masked=None,
+                query_mask=None, pool_tokens=0)
+    base.update(BAD_TREES[case])
+    _raises("PST_E_INVALID_TREE", pst.Tree, base["parent"], base["kv_offset"], base["kv_len"], base["query_node"],
+            num_q_heads=2, num_kv_heads=1, head_dim=64, dtype="f32", node_masked=base["node_masked"],
+            query_mask=base["query_mask"], pool_tokens=base["pool_tokens"], host_only=True)
+
+
+@pytest.mark.parametrize("hq,hkv,d,dt,odt", [(3, 2, 64, "f32", None), (4, 4, 96, "f32", None),
+                                             (4, 4, 64, "f32", "bf16"), (512, 1, 128, "bf16", None)])
+def test_unsupported_shape(hq, hkv, d, dt, odt):
+    _raises("PST_E_UNSUPPORTED", pst.Tree, [-1], [0], [5], [0], num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+            dtype=dt, out_dtype=odt, host_only=True)
+
+
+def test_bad_cost_tables():
+    _raises("PST_E_INVALID_ARG", pst.CostModel, ROWS, LENS, [[0] * 13] * 9)
+    bad = _table("affine")
+    bad[2][5] = 1
+    _raises("PST_E_INVALID_ARG", pst.CostModel, ROWS, LENS, bad)
+    _raises("PST_E_INVALID_ARG", pst.CostModel, [1, 1], LENS, _table("affine")[:2])
+
+
+def test_bad_plan_options():
+    t = _tree(workloads.config("1"))
+    _raises("PST_E_INVALID_ARG", pst.Plan, t, tile=100, host_only=True)
+    _raises("PST_E_INVALID_ARG", pst.Plan, t, max_rows=512, host_only=True)
+    _raises("PST_E_INVALID_ARG", pst.Plan, t, fixed_chunk=70, host_only=True)
+    _raises("PST_E_UNSUPPORTED", pst.Plan, t, max_rows=64, host_only=True)  # float32 rows > 16
+
+
+def test_host_only_objects_cannot_launch():
+    import torch
+
+    t = _tree(workloads.config("1"))
+    p = pst.Plan(t, num_bins=4, host_only=True)
+    x = torch.zeros(16)
+    e = _raises("PST_E_NO_DEVICE", pst.decode_attn, p, x, x, x, out=x, lse=x, ws=torch.zeros(4096, dtype=torch.uint8))
+    assert "host-only" in str(e)
+
+
+def test_free_order_and_lengths():
+    spec = workloads.config("3")
+    t = _tree(spec)
+    p = pst.Plan(t, num_bins=8, host_only=True)
+    _raises("PST_E_INVALID_ARG", t.free)  # a plan still borrows the tree
+    shorter = spec.kv_len.copy()
+    shorter[5] -= 1
+    _raises("PST_E_INVALID_ARG", t.set_lengths, shorter)
+    longer = spec.kv_len.copy()
+    longer[-1] += 10
+    _raises("PST_E_INVALID_TREE", t.set_lengths, longer)  # leaves the pool (pool = exact size)
+    p.free()
+    t.free()
+
+
+def test_growth_keeps_plan_and_updates_visible():
+    spec = workloads.config("2")
+    pool = spec.total_tokens + 1000
+    # Leaves are contiguous: give the last leaf room to grow inside a larger pool.
+    t = pst.Tree.from_spec(spec, host_only=True, pool_tokens=pool)
+    p = pst.Plan(t, num_bins=32, host_only=True)
+    before = p.view()
+    lens = spec.kv_len.copy()
+    lens[-1] += 7
+    t.set_lengths(lens)
+    assert t.index()["visible"][-1] == 32768 + 512 + 7
+    assert np.array_equal(p.view()["tasks"], before["tasks"])  # the plan is reused as is
+
+
+def test_empty_batch():
+    t = pst.Tree([-1], [0], [10], [], num_q_heads=4, num_kv_heads=4, head_dim=64, dtype="f32", host_only=True)
+    p = pst.Plan(t, num_bins=4, host_only=True)
+    v = p.view()
+    assert v["tasks"].shape == (0, 8) and v["num_slots"] == 0 and p.workspace_bytes == 0
