@@ -159,13 +159,24 @@ def test_bad_plan_options():
 
 
 def test_host_only_objects_cannot_launch():
+    import ctypes as C
+
+    t = _tree(workloads.config("1"))
+    p = pst.Plan(t, num_bins=4, host_only=True)
+    dummy = C.c_void_p(4096)  # never dereferenced: the call fails before any launch
+    st = pst._lib.pst_decode_attn(p._h, dummy, dummy, dummy, dummy, None, dummy, 1 << 20, None)
+    assert pst.STATUS[st] == "PST_E_NO_DEVICE"
+    assert "host-only" in pst._lib.pst_last_error().decode()
+
+
+def test_binding_rejects_host_tensors():
     import torch
 
     t = _tree(workloads.config("1"))
     p = pst.Plan(t, num_bins=4, host_only=True)
-    x = torch.zeros(16)
-    e = _raises("PST_E_NO_DEVICE", pst.decode_attn, p, x, x, x, out=x, lse=x, ws=torch.zeros(4096, dtype=torch.uint8))
-    assert "host-only" in str(e)
+    x = torch.zeros(4 * 4 * 64)
+    with pytest.raises(ValueError):
+        pst.decode_attn(p, x, x, x, out=x, lse=None, ws=torch.zeros(4096, dtype=torch.uint8))
 
 
 def test_free_order_and_lengths():
