@@ -31,6 +31,15 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python -m prefix_shared_tree_amd.build` "
         "(the HIP library is required; there is no fallback path)")
 
+# libpst.so links against libamdhip64.so.7.  PyTorch ships its own HIP
+# runtime under the same soname: importing torch first makes the library bind
+# to that one, so device pointers and stream handles from torch are valid in
+# the library (one HIP runtime per process).
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:  # pragma: no cover - torch is the memory/stream plumbing
+    _torch = None
+
 _lib = C.CDLL(LIB_PATH)
 
 PST_F32, PST_BF16 = 0, 1
@@ -181,6 +190,8 @@ class Tree:
         self.out_dtype = self.in_dtype if out_dtype is None else _dtype_code(out_dtype)
         shape = _Shape(num_q_heads, num_kv_heads, head_dim, self.in_dtype, self.out_dtype, scale,
                        kv_stride_head, kv_stride_token, pool_tokens)
+        if not host_only:
+            _init_device()
         strm = C.c_void_p(0) if host_only else _stream(stream)
         _check(_lib.pst_tree_build(C.byref(desc), C.byref(shape), TREE_HOST_ONLY if host_only else 0, strm,
                                    C.byref(self._h)))
@@ -378,7 +389,14 @@ def por(plan: Plan, out, lse, ws, stream=None):
     _check(_lib.pst_por(plan._h, _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def _init_device():
+    """Let torch initialise its HIP state before the library makes its first device call."""
+    if _torch is not None and _torch.cuda.is_available():
+        _torch.cuda.init()
+
+
 def device_info():
+    _init_device()
     cu, per = C.c_int32(), C.c_int32()
     _check(_lib.pst_device_info(C.byref(cu), C.byref(per)))
     return cu.value, per.value

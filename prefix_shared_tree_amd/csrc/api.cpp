@@ -76,6 +76,7 @@ struct pst_tree_s {
   int device = -1;
   uint64_t generation = 0;  // bumped when the device index is rebuilt
   int live_plans = 0;
+  std::vector<pst_plan_s*> plans;  // live plans: their device tasks follow length changes
   int64_t* d_node_off = nullptr;
   int32_t* d_node_len = nullptr;
   uint8_t* d_node_masked = nullptr;
@@ -91,10 +92,11 @@ struct pst_plan_s {
   PlanOptions opts;
   PlanResult r;
   bool on_device = false;
-  Task* d_tasks = nullptr;
+  DevTask* d_tasks = nullptr;
   int32_t* d_bin_ptr = nullptr;
   int32_t* d_entry_slot = nullptr;
   int64_t* d_slot_ptr = nullptr;
+  std::vector<DevTask> dev_tasks;  // host copy of d_tasks
 };
 
 struct pst_cost_s {
@@ -267,11 +269,27 @@ pst_status pst_tree_set_lengths(pst_tree_t t, const int32_t* kv_len, void* strea
     ix.visible[r] = vis;
   }
   std::copy(kv_len, kv_len + ix.N, ix.kv_len.begin());
+  hipStream_t s = static_cast<hipStream_t>(stream);
   if (t->on_device && ix.N > 0) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipMemcpyAsync(t->d_node_len, ix.kv_len.data(), ix.N * sizeof(int32_t), hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail("hipMemcpyAsync", e);
-    e = hipStreamSynchronize(s);
+  }
+  // The last piece of every node absorbs the growth: patch the plans' tasks.
+  for (pst_plan_s* p : t->plans) {
+    for (size_t i = 0; i < p->r.tasks.size(); ++i) {
+      const Task& a = p->r.tasks[i];
+      if (!(a.flags & PST_TASK_LAST_PIECE)) continue;
+      const int32_t len = ix.kv_len[a.node] - a.kv_begin;
+      if (i < p->dev_tasks.size()) p->dev_tasks[i].kv_len = len;
+    }
+    if (p->on_device && !p->dev_tasks.empty()) {
+      hipError_t e = hipMemcpyAsync(p->d_tasks, p->dev_tasks.data(), p->dev_tasks.size() * sizeof(DevTask),
+                                    hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return hip_fail("hipMemcpyAsync", e);
+    }
+  }
+  if (t->on_device) {
+    hipError_t e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail("hipStreamSynchronize", e);
   }
   return PST_OK;
@@ -443,7 +461,23 @@ pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* op
   if (!host_only) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::vector<int32_t> es32(p->r.entry_slot.begin(), p->r.entry_slot.end());
-    st = dev_upload(&p->d_tasks, p->r.tasks.data(), p->r.tasks.size(), s);
+    std::vector<DevTask>& dt = p->dev_tasks;
+    dt.resize(p->r.tasks.size());
+    for (size_t i = 0; i < dt.size(); ++i) {
+      const Task& a = p->r.tasks[i];
+      DevTask& b = dt[i];
+      b.tok0 = t->ix.kv_offset[a.node] + a.kv_begin;
+      b.node = a.node;
+      b.kv_begin = a.kv_begin;
+      b.kv_len = a.kv_len;
+      b.e0 = t->ix.nq_ptr[a.node];
+      b.row_begin = a.row_begin;
+      b.row_count = a.row_count;
+      b.piece = a.piece;
+      b.flags = ((a.flags & PST_TASK_LAST_PIECE) ? kDevLast : 0) | (t->ix.masked[a.node] ? kDevMasked : 0);
+      b.reserved = 0;
+    }
+    st = dev_upload(&p->d_tasks, dt.data(), dt.size(), s);
     if (st == PST_OK) st = dev_upload(&p->d_bin_ptr, p->r.bin_ptr.data(), p->r.bin_ptr.size(), s);
     if (st == PST_OK) st = dev_upload(&p->d_entry_slot, es32.data(), es32.size(), s);
     if (st == PST_OK) st = dev_upload(&p->d_slot_ptr, p->r.slot_ptr.data(), p->r.slot_ptr.size(), s);
@@ -459,6 +493,7 @@ pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* op
     p->on_device = true;
   }
   t->live_plans++;
+  t->plans.push_back(p);
   *out = p;
   return PST_OK;
 }
@@ -554,13 +589,9 @@ pst_status pst_pac(pst_plan_t p, const void* q, const void* k, const void* v, vo
   pp.lsepart = reinterpret_cast<float*>(static_cast<char*>(ws) + ob);
   pp.tasks = p->d_tasks;
   pp.bin_ptr = p->d_bin_ptr;
-  pp.node_off = t->d_node_off;
-  pp.node_len = t->d_node_len;
-  pp.nq_ptr = t->d_nq_ptr;
   pp.nq_idx = t->d_nq_idx;
   pp.nq_mask = t->d_nq_mask;
   pp.entry_slot = p->d_entry_slot;
-  pp.node_masked = t->d_node_masked;
   pp.stride_head = t->shape.kv_stride_head;
   pp.stride_token = t->shape.kv_stride_token;
   pp.num_bins = p->opts.m;
@@ -620,7 +651,11 @@ pst_status pst_free(void* obj) {
   }
   if (magic == kPlanMagic) {
     pst_plan_s* p = static_cast<pst_plan_s*>(obj);
-    if (p->tree) p->tree->live_plans--;
+    if (p->tree) {
+      p->tree->live_plans--;
+      auto& v = p->tree->plans;
+      v.erase(std::remove(v.begin(), v.end(), p), v.end());
+    }
     free_plan_device(p);
     p->magic = 0;
     delete p;

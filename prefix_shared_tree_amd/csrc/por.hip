@@ -11,7 +11,7 @@
 //     L* = max_i LSE_i,  w_i = exp(LSE_i - L*),
 //     O = sum_i w_i O_i / sum_i w_i,  LSE = L* + ln sum_i w_i,
 // which is the binary POR folded over the chain; empty partials (LSE = -inf)
-// get weight 0.  One workgroup per query; threads own (q-head, 4 channels).
+// get weight 0.  Each thread owns one chain: (query, q-head, 4 channels).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -28,12 +28,16 @@ constexpr int kPorThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
+// Grid: (query, chunk of kPorThreads (head, 4-channel) pairs).
 template <int D, bool BF16_OUT>
-__global__ __launch_bounds__(kPorThreads) void por_kernel(PorParams p) {
-  const int r = blockIdx.x;
+__global__ __launch_bounds__(kPorThreads) void por_kernel(PorParams p, int chunks) {
+  const int r = blockIdx.x / chunks;
+  const int chunk = blockIdx.x % chunks;
   const int64_t s0 = p.slot_ptr[r], s1 = p.slot_ptr[r + 1];
   constexpr int C4 = D / 4;
-  for (int idx = threadIdx.x; idx < p.hq * C4; idx += kPorThreads) {
+  {
+    const int idx = chunk * kPorThreads + threadIdx.x;
+    if (idx >= p.hq * C4) return;
     const int h = idx / C4, c4 = idx % C4;
     float lmax = kNegInf;
     for (int64_t s = s0; s < s1; ++s) lmax = fmaxf(lmax, p.lsepart[s * p.hq + h]);
@@ -100,18 +104,19 @@ __global__ __launch_bounds__(256) void read_kernel(const uint4* buf, size_t n16,
 
 int launch_por(const PorParams& p, int head_dim, int out_dtype, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(p.num_queries), block(kPorThreads);
+  const int chunks = (p.hq * (head_dim / 4) + kPorThreads - 1) / kPorThreads;
+  const dim3 grid(static_cast<unsigned>(p.num_queries) * chunks), block(kPorThreads);
   const bool bf = out_dtype == PST_BF16;
   if (head_dim == 128) {
     if (bf)
-      hipLaunchKernelGGL((por_kernel<128, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((por_kernel<128, true>), grid, block, 0, s, p, chunks);
     else
-      hipLaunchKernelGGL((por_kernel<128, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((por_kernel<128, false>), grid, block, 0, s, p, chunks);
   } else {
     if (bf)
-      hipLaunchKernelGGL((por_kernel<64, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((por_kernel<64, true>), grid, block, 0, s, p, chunks);
     else
-      hipLaunchKernelGGL((por_kernel<64, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((por_kernel<64, false>), grid, block, 0, s, p, chunks);
   }
   return static_cast<int>(hipGetLastError());
 }

@@ -36,6 +36,23 @@ struct Task {
 };
 static_assert(sizeof(Task) == 32, "task layout");
 
+// What the kernel reads per piece (built from a Task and the tree's node table).
+struct DevTask {
+  int64_t tok0;     // first token of the piece in the K/V pools
+  int32_t node;
+  int32_t kv_begin;
+  int32_t kv_len;   // tokens (kept current for a growing last piece by pst_tree_set_lengths)
+  int32_t e0;       // first node->query entry of the node
+  int32_t row_begin;
+  int32_t row_count;
+  int32_t piece;
+  int32_t flags;    // kDevLast | kDevMasked
+  int64_t reserved;
+};
+static_assert(sizeof(DevTask) == 48, "device task layout");
+constexpr int32_t kDevLast = 1;
+constexpr int32_t kDevMasked = 2;
+
 struct CostModel {
   uint32_t magic = kCostMagic;
   std::vector<int32_t> rows_grid;
@@ -90,15 +107,11 @@ struct PacParams {
   const void* v;
   float* opart;    // [slots][hq][d]
   float* lsepart;  // [slots][hq]
-  const Task* tasks;
+  const DevTask* tasks;
   const int32_t* bin_ptr;
-  const int64_t* node_off;
-  const int32_t* node_len;
-  const int32_t* nq_ptr;
   const int32_t* nq_idx;
   const uint64_t* nq_mask;
   const int32_t* entry_slot;
-  const uint8_t* node_masked;
   int64_t stride_head;   // elements
   int64_t stride_token;  // elements
   int32_t num_bins;
