@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--config", default="2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline", action="store_true", help="skip the query-guided comparison")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the warm-cache timing (every PAC launch of the run is then cold, as under a profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "pac_traffic.json"),
                     help="rocprofv3 counter summary giving the PAC kernel's HBM bytes")
@@ -134,8 +136,8 @@ def cpu_baseline(spec, q, k, v, out, budget_s):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}); "
-              "see DESIGN.md for how the path would shard.", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {a.gpus}); "
+              "sharding across GPUs is a design, not code.", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -163,7 +165,7 @@ def main():
     step_ms = [x + y for x, y in zip(pac_ms, por_ms)]
     ms = statistics.mean(step_ms)
     pac_avg = statistics.mean(pac_ms)
-    warm_ms = time_warm(torch, pst, plan, q, k, v, out, lse, ws, a.steps)
+    warm_ms = None if a.no_warm else time_warm(torch, pst, plan, q, k, v, out, lse, ws, a.steps)
 
     # Achievable streaming read bandwidth (same 128-bit loads, 2 GiB).
     rd = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
@@ -233,6 +235,7 @@ def main():
         }
         del bws
         # The tree path's output is recomputed below for the parity sample.
+    pst.bench_flush(flush)
     pst.decode_attn(plan, q, k, v, out=out, lse=lse, ws=ws)
     torch.cuda.synchronize()
     if not a.no_cpu_baseline:

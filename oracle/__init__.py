@@ -19,7 +19,7 @@ Contents (each function cites the passage it follows):
   node->query CSR) in canonical order.
 * :mod:`oracle.cost` and :mod:`oracle.planner` -- integer cost-table lookup
   and the task partitioner, as read from CoDec's workload-balance section;
-  the pages leave the exact procedure open, so these follow this build's
+  the pages leave the exact procedure open, so these follow the library's
   stated reading step by step.
 
 Parity status: attention, merge and index are pinned by tests against

@@ -14,7 +14,7 @@ grid-searches the split per node.  The assignment step is list scheduling
 the longest-processing-time order is used.
 
 The pages fix no constants, tie-breaks or piece geometry.  This is the
-reading this build implements identically in the library, all in integers:
+reading taken here, implemented identically in the library, all in integers:
 
 1. rows r_i = n_q[i] * g (queries x GQA group).  If r_i > R_max the rows are
    cut into gq_i = ceil(r_i / R_max) row groups of ceil(r_i / gq_i) rows (the
