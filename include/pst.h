@@ -168,6 +168,9 @@ pst_status pst_cost_model_lookup(pst_cost_model_t cost, int32_t rows, int64_t le
 #define PST_PLAN_QUERY_GUIDED 1u /* FlashDecoding-style baseline: one query per row group (shared KV re-read per query) */
 #define PST_PLAN_NO_SPLIT 2u     /* every node is one piece (b_k = 1) */
 #define PST_PLAN_HOST_ONLY 4u    /* compute on the host only (no GPU needed) */
+#define PST_PLAN_DOT_SMALL 8u    /* bf16 pieces of fewer than 16 rows take the wavefront dot-product path
+                                    (the split CoDec and DEFT use); default: matrix cores for every bf16
+                                    piece, which streams faster on gfx950 even at 1 row of 16 */
 typedef struct {
   int32_t num_bins;    /* workgroups per kv head; 0 = resident capacity / num_kv_heads */
   int32_t max_rows;    /* rows one workgroup holds (R_max); 0 = 256 (bf16) or 16 (f32); <= 256 */
@@ -224,6 +227,7 @@ typedef struct {
   int64_t cost_l;                /* binary-search bound (0 for fixed geometries) */
   int32_t chosen_k;
   int32_t max_rows;
+  int32_t mfma_min_rows;         /* bf16 pieces with at least this many rows use the matrix cores */
 } pst_plan_view;
 pst_status pst_plan_get(pst_plan_t plan, pst_plan_view* view);
 

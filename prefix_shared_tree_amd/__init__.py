@@ -44,7 +44,7 @@ _lib = C.CDLL(LIB_PATH)
 
 PST_F32, PST_BF16 = 0, 1
 TREE_HOST_ONLY = 1
-PLAN_QUERY_GUIDED, PLAN_NO_SPLIT, PLAN_HOST_ONLY = 1, 2, 4
+PLAN_QUERY_GUIDED, PLAN_NO_SPLIT, PLAN_HOST_ONLY, PLAN_DOT_SMALL = 1, 2, 4, 8
 TASK_FIELDS = 8
 
 STATUS = {
@@ -96,7 +96,8 @@ class _PlanView(C.Structure):
                 ("tasks", C.c_void_p), ("bin_ptr", C.c_void_p), ("slot_ptr", C.c_void_p),
                 ("entry_slot", C.c_void_p), ("piece_len", C.c_void_p), ("b_eff", C.c_void_p),
                 ("rows_per_group", C.c_void_p), ("bin_load", C.c_void_p), ("makespan", C.c_int64),
-                ("cost_l", C.c_int64), ("chosen_k", C.c_int32), ("max_rows", C.c_int32)]
+                ("cost_l", C.c_int64), ("chosen_k", C.c_int32), ("max_rows", C.c_int32),
+                ("mfma_min_rows", C.c_int32)]
 
 
 _P = C.c_void_p
@@ -281,13 +282,13 @@ class Plan:
 
     def __init__(self, tree: Tree, cost: Optional[CostModel] = None, *, num_bins=0, max_rows=0, tile=0,
                  grid_steps=0, fixed_chunk=0, query_guided=False, no_split=False, host_only=False, stream=None,
-                 use_fitted=True):
+                 use_fitted=True, dot_small=False):
         self.tree = tree
         if cost is None and use_fitted:
             cost = default_cost_model(tree.head_dim, tree.num_q_heads, tree.num_kv_heads, tree.in_dtype)
         self.cost = cost
         flags = (PLAN_QUERY_GUIDED if query_guided else 0) | (PLAN_NO_SPLIT if no_split else 0) | \
-                (PLAN_HOST_ONLY if host_only else 0)
+                (PLAN_HOST_ONLY if host_only else 0) | (PLAN_DOT_SMALL if dot_small else 0)
         opts = _PlanOpts(num_bins, max_rows, tile, grid_steps, fixed_chunk, flags)
         self._h = C.c_void_p()
         host = host_only or tree.host_only
@@ -302,7 +303,7 @@ class Plan:
         _check(_lib.pst_plan_get(self._h, C.byref(v)))
         return {
             "num_bins": v.num_bins, "num_slots": v.num_slots, "makespan": v.makespan, "cost_l": v.cost_l,
-            "chosen_k": v.chosen_k, "max_rows": v.max_rows,
+            "chosen_k": v.chosen_k, "max_rows": v.max_rows, "mfma_min_rows": v.mfma_min_rows,
             "tasks": _view(v.tasks, v.num_tasks * TASK_FIELDS, np.int32).reshape(-1, TASK_FIELDS),
             "bin_ptr": _view(v.bin_ptr, v.num_bins + 1, np.int32),
             "slot_ptr": _view(v.slot_ptr, v.num_queries + 1, np.int64),

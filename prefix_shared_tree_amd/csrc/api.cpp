@@ -407,6 +407,7 @@ pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* op
   po.fixed_chunk = o.fixed_chunk;
   po.no_split = (o.flags & PST_PLAN_NO_SPLIT) != 0;
   po.query_guided = (o.flags & PST_PLAN_QUERY_GUIDED) != 0;
+  po.mfma_min_rows = (o.flags & PST_PLAN_DOT_SMALL) ? kMfmaMinRowsDot : 1;
   const int32_t default_rows = t->shape.in_dtype == PST_F32 ? kMaxRowsDot : kMaxRows;
   po.r_max = o.max_rows > 0 ? o.max_rows : default_rows;
   if (po.tile % kTile != 0 || po.r_max > kMaxRows || po.fixed_chunk < 0 || po.fixed_chunk % kTile != 0 ||
@@ -540,6 +541,7 @@ pst_status pst_plan_get(pst_plan_t p, pst_plan_view* v) {
   v->cost_l = p->r.cost_l;
   v->chosen_k = p->r.chosen_k;
   v->max_rows = p->opts.query_guided ? p->tree->shape.num_q_heads / p->tree->shape.num_kv_heads : p->opts.r_max;
+  v->mfma_min_rows = p->tree->shape.in_dtype == PST_BF16 ? p->opts.mfma_min_rows : INT32_MAX;
   return PST_OK;
 }
 
@@ -598,6 +600,7 @@ pst_status pst_pac(pst_plan_t p, const void* q, const void* k, const void* v, vo
   pp.hq = t->shape.num_q_heads;
   pp.hkv = t->shape.num_kv_heads;
   pp.g = pp.hq / pp.hkv;
+  pp.mfma_min_rows = p->opts.mfma_min_rows;
   pp.scale_log2 = t->shape.scale * 1.4426950408889634f;
   int e = launch_pac(pp, t->shape.in_dtype, t->shape.head_dim, stream);
   if (e != 0) return hip_fail("PAC launch", static_cast<hipError_t>(e));

@@ -730,7 +730,7 @@ __global__ __launch_bounds__(kPacThreads) void pac_kernel(PacParams p) {
     t.vbase = static_cast<const char*>(p.v) + off;
     bool done = false;
     if constexpr (sizeof(T) == 2) {
-      if (t.row_count >= kMfmaMinRows) {
+      if (t.row_count >= p.mfma_min_rows) {
         mfma_piece<D>(p, t, kvh);
         done = true;
       }

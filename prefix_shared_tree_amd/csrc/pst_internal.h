@@ -16,7 +16,7 @@ constexpr uint32_t kCostMagic = 0x33545350u;  // "PST3"
 
 constexpr int kTile = 64;         // tokens per K/V tile of the partial-attention kernel
 constexpr int kMaxRows = 256;     // rows one workgroup holds (MFMA path: 8 waves x 32 rows)
-constexpr int kMfmaMinRows = 16;  // rows from which a bf16 piece uses the matrix cores
+constexpr int kMfmaMinRowsDot = 16;  // matrix-core threshold with PST_PLAN_DOT_SMALL (else 1)
 constexpr int kMaxRowsDot = 16;   // the dot-product path keeps up to this many rows in registers
 constexpr int kPacThreads = 512;  // 8 wavefronts of 64
 
@@ -83,6 +83,7 @@ struct PlanOptions {
   int32_t fixed_chunk = 0;
   bool no_split = false;
   bool query_guided = false;
+  int32_t mfma_min_rows = 1;
 };
 
 struct PlanResult {
@@ -118,7 +119,8 @@ struct PacParams {
   int32_t hq;
   int32_t hkv;
   int32_t g;
-  float scale_log2;  // scale * log2(e)
+  int32_t mfma_min_rows;  // bf16 pieces with at least this many rows use the matrix cores
+  float scale_log2;       // scale * log2(e)
 };
 
 struct PorParams {

@@ -10,7 +10,9 @@ the plan forced to one piece per node and k nodes per bin: every workgroup of
 a full-GPU launch runs k pieces of `rows` query rows and `len` tokens, on a
 loaded GPU (shared HBM bandwidth included), caches flushed before every
 launch.  The cost of a piece is the marginal time (T(k) - T(1)) / (k - 1), so
-the launch itself, paid once per launch and not per piece, is left out.  The
+the launch itself, paid once per launch and not per piece, is left out.
+Caches are emptied by reading 1 GiB of an unrelated buffer (reads leave no
+dirty lines whose write-back would be charged to the measured launch).  The
 table is made non-decreasing along both axes and written as JSON:
 
     python -m prefix_shared_tree_amd.fit_cost --q-heads 32 --kv-heads 8 --head-dim 128 --dtype bf16
@@ -57,7 +59,7 @@ def measure(pst, torch, hq, hkv, d, dtype, rows, length, bins, reps, flush, per_
     stream = torch.cuda.current_stream()
     times = []
     for i in range(reps + 1):
-        pst.bench_flush(flush)
+        pst.bench_read(flush[0], flush[1])
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         pst.pac(plan, q, k, v, ws)
@@ -88,7 +90,7 @@ def main():
     g = hq // hkv
     cus, per = pst.device_info()
     bins = max(1, cus * per // hkv)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = (torch.empty(1 << 30, dtype=torch.uint8, device="cuda"), torch.empty(4096, dtype=torch.float32, device="cuda"))
     rows_max = 256 if a.dtype == "bf16" else 16
     raw = {}
     launch = []

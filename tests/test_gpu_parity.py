@@ -108,7 +108,7 @@ def test_random_trees(seed):
                                      num_kv_heads=hkv, head_dim=d, dtype=dtype)
     say(f"random tree seed {seed}: dtype {spec.dtype} H {spec.num_q_heads}/{spec.num_kv_heads} d {spec.head_dim} "
         f"N {spec.num_nodes} B {spec.num_queries}")
-    t, plan, out, lse = run(spec, num_bins=int(rng.choice([0, 3, 17])))
+    t, plan, out, lse = run(spec, num_bins=int(rng.choice([0, 3, 17])), dot_small=seed % 2 == 1)
     check(spec, t, out, lse)
 
 
@@ -119,6 +119,17 @@ def test_row_counts_single_node(rows):
                               rows, 1, 128, "bf16", 77)
     say(f"rows {rows}")
     t, plan, out, lse = run(spec, num_bins=5)
+    check(spec, t, out, lse)
+
+
+@pytest.mark.parametrize("rows", [1, 2, 4, 8, 12, 15])
+def test_row_counts_dot_path(rows):
+    """The wavefront dot-product path for bf16 pieces below 16 rows (PST_PLAN_DOT_SMALL)."""
+    spec = workloads.TreeSpec(f"rows{rows}-dot", np.array([-1]), np.array([1000]), np.array([0]), np.array([0]),
+                              rows, 1, 128, "bf16", 78)
+    say(f"rows {rows} on the dot-product path")
+    t, plan, out, lse = run(spec, num_bins=5, dot_small=True)
+    assert plan.view()["mfma_min_rows"] == 16
     check(spec, t, out, lse)
 
 

@@ -158,6 +158,16 @@ def test_bad_plan_options():
     _raises("PST_E_UNSUPPORTED", pst.Plan, t, max_rows=64, host_only=True)  # float32 rows > 16
 
 
+def test_engine_threshold():
+    """bf16 plans put every piece on the matrix cores unless PST_PLAN_DOT_SMALL asks for the
+    dot-product path below 16 rows; float32 plans never use them."""
+    t = _tree(workloads.config("3"))
+    assert pst.Plan(t, num_bins=8, host_only=True).view()["mfma_min_rows"] == 1
+    assert pst.Plan(t, num_bins=8, host_only=True, dot_small=True).view()["mfma_min_rows"] == 16
+    t1 = _tree(workloads.config("1"))
+    assert pst.Plan(t1, num_bins=4, host_only=True).view()["mfma_min_rows"] == 2**31 - 1
+
+
 def test_host_only_objects_cannot_launch():
     import ctypes as C
 
