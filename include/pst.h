@@ -240,7 +240,7 @@ pst_status pst_plan_get(pst_plan_t plan, pst_plan_view* view);
  *   workspace device, >= pst_plan_workspace_size bytes, 256-byte aligned
  * Returns PST_E_PLAN_STALE if the tree was rebuilt under the plan,
  * PST_E_WORKSPACE if the workspace is missing or short, PST_E_NO_DEVICE for
- * host-only objects. */
+ * host-only objects, PST_E_UNSUPPORTED if q spans more than 2^31 - 1 bytes. */
 pst_status pst_decode_attn(pst_plan_t plan, const void* q, const void* k_pool, const void* v_pool,
                            void* out, float* lse_out, void* workspace, size_t workspace_bytes,
                            void* stream);

@@ -596,6 +596,12 @@ pst_status pst_pac(pst_plan_t p, const void* q, const void* k, const void* v, vo
   pp.entry_slot = p->d_entry_slot;
   pp.stride_head = t->shape.kv_stride_head;
   pp.stride_token = t->shape.kv_stride_token;
+  pp.q_bytes = static_cast<int64_t>(t->ix.B) * t->shape.num_q_heads * t->shape.head_dim *
+               elem_bytes(t->shape.in_dtype);
+  if (pp.q_bytes > INT32_MAX) {
+    set_error("the query tensor exceeds 2 GiB (gathered with 32-bit offsets)");
+    return PST_E_UNSUPPORTED;
+  }
   pp.num_bins = p->opts.m;
   pp.hq = t->shape.num_q_heads;
   pp.hkv = t->shape.num_kv_heads;

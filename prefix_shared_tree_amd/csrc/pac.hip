@@ -16,29 +16,33 @@
 // rows of a node are (node->query entry, head of the GQA group).
 //
 // Memory pipeline (both paths): the piece's K and V stream through LDS in
-// 16 KB tiles (64 tokens at d = 128 bf16) by direct HBM->LDS DMA
+// 16 KB half-tiles (64 tokens at d = 128 bf16) by direct HBM->LDS DMA
 // (buffer_load_dwordx4 ... lds), four stages deep, so three tiles are in
 // flight while one is computed and no registers hold staged data.  Rows are
 // XOR-swizzled by 16-byte chunk so the reads below spread over the banks;
 // loads past the piece end return zeros.
 //
 // Two compute paths, chosen per piece:
-//  * matrix cores (bf16, >= 16 rows): each wavefront owns 16 or 32 rows and
-//    half or all of each tile's tokens and computes S^T = K Q^T and
-//    O^T += V^T P^T with v_mfma_f32_16x16x32_bf16, so every row's softmax
-//    state stays in one lane.  V^T fragments come straight from the row-major
-//    tile with the LDS transpose read ds_read_b64_tr_b16.  P enters the MFMA
-//    as a bf16 hi/lo pair so its rounding stays near float32;
-//  * wavefront dot products (fewer rows, or float32): groups of
-//    head_dim*elem/16 lanes take one token each, reduce q.k across the group
-//    with DPP, and keep a running (max, sum, O) per row; states are merged
-//    across lane groups and wavefronts at the end of the piece.
+//  * matrix cores (every bf16 piece by default): each wavefront owns 16 or 32
+//    rows and half or all of each tile's tokens and computes S^T = K Q^T
+//    (v_mfma_f32_16x16x32_bf16) and O^T += V^T P^T (v_mfma_f32_16x16x32_f16),
+//    so every row's softmax state stays in one lane.  V^T fragments come
+//    straight from the row-major tile with the LDS transpose read
+//    ds_read_b64_tr_b16.  The product O += P V of a tile runs one tile late,
+//    next to the next tile's softmax, so matrix cores and vector ALU overlap;
+//    for it each V tile is converted once in LDS to fp16 (scaled by 2^-8) and
+//    P is rounded to fp16;
+//  * wavefront dot products (float32, or bf16 pieces below 16 rows on
+//    request): groups of head_dim*elem/16 lanes take one token each, reduce
+//    q.k across the group with DPP, and keep a running (max, sum, O) per row;
+//    states are merged across lane groups and wavefronts at the end.
 // Both use the streaming softmax of CoDec section KV缓存管理 (per-block
 // maximum, rescale of the running sum and numerator at the common maximum)
 // in base 2, and emit the normalised partial O and its natural-log LSE.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "pst_internal.h"
 
@@ -50,6 +54,8 @@ typedef short bf16x4s __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2n __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 constexpr int NW = kPacThreads / 64;  // wavefronts per workgroup
@@ -60,9 +66,15 @@ constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazy = 8.0f;  // log2 headroom before the reference maximum is raised
 constexpr size_t kTileBytes = static_cast<size_t>(NSTAGE) * STAGE_BYTES;  // 128 KB of tile stages
-constexpr size_t kAuxBytes = 8 * 1024;  // softmax states exchanged between wavefronts
-constexpr size_t kLdsBytes = kTileBytes + kAuxBytes;
+// The aggregated queries of a matrix-core piece (up to 256 rows x 256 B)
+// arrive in the V half of stage 2, stage 3 and 16 KB after the stages: the
+// tile schedule refills none of them before the queries are in registers.
+constexpr size_t kQOff = 2 * STAGE_BYTES + TILE_BYTES;
+constexpr size_t kAuxOff = kQOff + 64 * 1024;
+constexpr size_t kAuxBytes = 8 * 1024;  // softmax states exchanged between wavefronts; next task record
+constexpr size_t kLdsBytes = kAuxOff + kAuxBytes;
 static_assert(kTileBytes >= 64 * 1024, "merge scratch reuses the tile stages");
+static_assert(kLdsBytes <= 160 * 1024, "one workgroup per compute unit");
 
 // The workgroup's LDS (dynamic size kLdsBytes), visible to every path as LDS.
 extern __shared__ __attribute__((aligned(16))) char pac_lds[];
@@ -74,14 +86,24 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// max(a, b, c).  Plain fmaxf: this file is compiled with IEEE mode off, so
+// no quieting moves precede it and the compiler fuses pairs into v_max3.
+// (Inline assembly must not be used here: the compiler inserts no wait
+// states between a matrix-core result and an assembly statement reading it.)
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // Raw buffer over [base, base + bytes): loads past the end return zeros, so
 // the ragged tail of a piece needs no branch.  Rebased per tile so the 32-bit
 // offsets stay small whatever the pool size.
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit data format for gfx9-family buffer descriptors
+// Callers pass wave-uniform values; they are re-read as such so that the
+// descriptor lives in scalar registers (the DMA takes it as an SGPR operand).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t bytes) {
-  const int n = bytes > 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes < 0 ? 0 : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), static_cast<short>(0), n, kBufferWord3);
+  const int n = __builtin_amdgcn_readfirstlane(bytes > 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes < 0 ? 0 : bytes));
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t u = static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)))) |
+                     (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)))) << 32);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char*>(u), static_cast<short>(0), n, kBufferWord3);
 }
 
 // One 16-byte-per-lane HBM->LDS DMA: LDS destination = lds_addr + 16 * lane.
@@ -101,6 +123,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, uint32
       : "=&s"(saved)
       : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
       : "memory");
+}
+// threadIdx.x through an opaque move: values derived from it inside a piece
+// are recomputed per piece instead of being hoisted out of the piece loop and
+// held in registers across every piece.
+__device__ __forceinline__ int piece_tid() {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(static_cast<int>(threadIdx.x)));
+  return t;
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
@@ -175,7 +205,7 @@ __device__ __forceinline__ void issue_tile(const TaskInfo& t, int64_t stb, int t
   const int64_t bytes = static_cast<int64_t>(min(G::TT, t.kv_len - tok_base)) * stb;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(t.kbase + tok_base * stb, bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(t.vbase + tok_base * stb, bytes);
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   char* st = pac_lds + stage * STAGE_BYTES;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
@@ -217,216 +247,403 @@ __device__ __forceinline__ void run_tiles(const TaskInfo& t, int64_t stb, int ti
 // ---------------------------------------------------------------------------
 // Matrix-core path (bf16)
 // ---------------------------------------------------------------------------
-// Each wavefront owns RBr blocks of 16 rows (RBr = 1 up to 64 rows, else 2)
-// of a slab; TS wavefronts share a slab (TS = 2 while there are at most 4
-// slabs), each taking TT/TS tokens of every tile in sub-steps of 32.
-// Registers are sized for RB = 2; the second block is skipped when RBr = 1.
+// O^T += V^T P^T runs in fp16: P <= 2^kLazy is rounded to nearest fp16
+// (2^-11 relative per weight, four times finer than bf16) and the row sums
+// add the same rounded P.  Each V tile is converted once in LDS, by all
+// threads together, from bf16 to fp16 scaled by 2^-8 (exact for |v| in
+// [2^-6, 2^23]; smaller values keep an absolute error below 2^-17, larger
+// ones saturate: round-toward-zero never overflows to infinity); the output
+// takes the 2^8 back when it is normalised.
+constexpr float kVScale = 0x1p-8f;
+
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  const f32x2 x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+}
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2_scaled(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(w) * kVScale, bf16_hi(w) * kVScale));
+}
+
+__device__ __forceinline__ char* kslot(int j) { return pac_lds + (j % NSTAGE) * STAGE_BYTES; }
+__device__ __forceinline__ char* vslot(int j) { return pac_lds + (j % NSTAGE) * STAGE_BYTES + TILE_BYTES; }
+
+// DMA of the K (or V) half of tile `tile` (16 KB) into `dst`: every wavefront
+// writes two 1 KB blocks; lane L of block b fills chunk position P = 64 b + L,
+// i.e. token P / CPT, chunk (P % CPT) ^ (token % CPT).
 template <int D>
+__device__ __forceinline__ void issue_half(const char* base, int kv_len, int64_t stb, int tile, char* dst, int tid) {
+  using G = Geo<D, 2>;
+  const int tok_base = tile * G::TT;
+  const int64_t bytes = static_cast<int64_t>(min(G::TT, kv_len - tok_base)) * stb;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base + tok_base * stb, bytes);
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int b = c * NW + w;
+    const int P = b * 64 + lane;
+    const int tok = P / G::CPT, phys = P % G::CPT;
+    dma16(r, static_cast<int>(tok * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4), lds_addr(dst + b * 1024));
+  }
+}
+
+// DMA schedule of a piece of nt tiles: group j holds K of tile j (j < nt)
+// and V of tile j - 1 (1 <= j <= nt), two operations per thread each.
+// Iteration i of the tile loop consumes group i (QK of tile i, PV of tile
+// i - 1) and issues group i + 3, so three groups stay in flight; K of tile
+// i + 3 refills the K half of tile i - 1 and V of tile i + 2 the V half of
+// tile i - 2, both finished before iteration i's barrier.
+__device__ __forceinline__ int group_ops(int j, int nt) { return (j < nt ? 2 : 0) + (j >= 1 && j <= nt ? 2 : 0); }
+
+// Wait until at most n (0..8) of this wavefront's vector memory operations are outstanding.
+__device__ __forceinline__ void wait_vmem_n(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+  }
+}
+__device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
+
+// Each wavefront owns RBR blocks of 16 rows of a slab; TS wavefronts share a
+// slab, each taking TT/TS tokens of every tile in NSUB = TT/(32 TS) sub-steps
+// of 32 tokens (a tile is 64 tokens at d = 128, 128 at d = 64).  The
+// sub-steps are software-pipelined: step k computes S = K Q^T and the
+// softmax of step k while the matrix cores run O += P V of step k - 1, so
+// matrix-core and vector work overlap inside a wavefront.
+template <int D, int RBR, int TS>
 __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t, int kvh) {
   using G = Geo<D, 2>;
-  char* const lds = pac_lds;
-  constexpr int RB = 2;
   constexpr int KS = D / 32;  // k-steps of S^T = K Q^T
   constexpr int DB = D / 16;  // d-blocks of O^T
-  const int RBr = t.row_count <= 64 ? 1 : 2;
-  const int ROWS_W = 16 * RBr;
-  const int slabs = (t.row_count + ROWS_W - 1) / ROWS_W;
-  const int TS = slabs <= 4 ? 2 : 1;
-  const int nsub = G::TT / (32 * TS);  // 32-token sub-steps per wavefront per tile
-  const int tid = threadIdx.x;
+  constexpr int NSUB = G::TT / (32 * TS);  // 32-token sub-steps per wavefront and tile
+  constexpr int ROWS_W = 16 * RBR;
+  constexpr int QOPS = kMaxRows * G::CPT / 64 / NW;  // Q DMA operations per thread at most
+  char* const lds = pac_lds;
+  const int tid = piece_tid();
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l16 = lane & 15, lg = lane >> 4;
+  const int R = t.row_count;
+  const int slabs = (R + ROWS_W - 1) / ROWS_W;
   const int slab = w / TS, half = w % TS;
   const bool active = slab < slabs;
   const int tok0 = half * (G::TT / TS);
   const int64_t stb = p.stride_token * 2;
+  const int nt = (t.kv_len + G::TT - 1) / G::TT;
+  const float c2 = p.scale_log2;
+  char* const qarea = lds + kQOff;
 
-  issue_prologue<D, 2>(t, stb, tid);
-
-  // Gather the aggregated queries: B operand fragments of Q^T.  Branch-free
-  // (dead rows read row 0 of the task and are zeroed) so that all index loads
-  // and then all query loads are in flight together.
-  bf16x8 qf[RB][KS];
-  bool qok[RB];
-  int qrow_off[RB], slot0[RB], qhead[RB];
+  // Gather offsets of the Q chunks this thread moves (rows past R read out
+  // of range: zeros), and the slot, head and mask of the rows this lane owns.
+  const int qops_total = (R * G::CPT + 63) / 64;
+  uint32_t qoff[QOPS];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
+  for (int o = 0; o < QOPS; ++o) {
+    const int P = (o * NW + w) * 64 + lane;
+    const int row = P / G::CPT, phys = P % G::CPT;
     int entry = t.e0 + t.row_begin / p.g, head = kvh * p.g + t.row_begin % p.g;
-    qok[rb] = active && rb < RBr && row_target(p, t, kvh, slab * ROWS_W + rb * 16 + l16, &entry, &head);
-    qrow_off[rb] = p.nq_idx[entry] * p.hq + head;
+    const bool ok = row_target(p, t, kvh, row, &entry, &head);
+    const uint32_t qrow = static_cast<uint32_t>(p.nq_idx[entry] * p.hq + head);
+    qoff[o] = ok ? qrow * G::ROWB + ((phys ^ (row & (G::CPT - 1))) << 4) : 0x80000000u;
+  }
+  bool qok[RBR];
+  int slot0[RBR], qhead[RBR];
+  uint64_t rmask[RBR];
+#pragma unroll
+  for (int rb = 0; rb < RBR; ++rb) {
+    int entry = t.e0 + t.row_begin / p.g, head = kvh * p.g + t.row_begin % p.g;
+    qok[rb] = active && row_target(p, t, kvh, slab * ROWS_W + rb * 16 + l16, &entry, &head);
     slot0[rb] = p.entry_slot[entry];
     qhead[rb] = head;
+    rmask[rb] = ~0ull;
+    if (t.masked && qok[rb]) rmask[rb] = p.nq_mask[entry];
   }
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + static_cast<int64_t>(qrow_off[rb]) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qrow + ks * 32 + lg * 8);
-      const uint4 z = make_uint4(qok[rb] ? v.x : 0u, qok[rb] ? v.y : 0u, qok[rb] ? v.z : 0u, qok[rb] ? v.w : 0u);
-      qf[rb][ks] = __builtin_bit_cast(bf16x8, z);
-    }
-  }
-  // The queries must be in registers before the tile loop: without this wait
-  // the compiler would wait for them (and every DMA behind them) inside it.
-  wait_vmem(0);
-  // Mask of a row (masked nodes only; read when needed).
-  auto row_mask = [&](int rb) -> uint64_t {
-    int entry = 0, head = 0;
-    if (!row_target(p, t, kvh, slab * ROWS_W + rb * 16 + l16, &entry, &head)) return ~0ull;
-    return p.nq_mask[entry];
-  };
 
-  f32x4 o[DB][RB];
-  float m[RB], l[RB];
+  // Queries first (needed first), then groups 0..2.
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const char*>(p.q), p.q_bytes);
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
+    for (int o = 0; o < QOPS; ++o)
+      if (o * NW + w < qops_total) dma16(rq, static_cast<int>(qoff[o]), lds_addr(qarea + (o * NW + w) * 1024));
+  }
+  if (0 < nt) issue_half<D>(t.kbase, t.kv_len, stb, 0, kslot(0), tid);
+  if (1 < nt) issue_half<D>(t.kbase, t.kv_len, stb, 1, kslot(1), tid);
+  if (0 < nt) issue_half<D>(t.vbase, t.kv_len, stb, 0, vslot(0), tid);
+  if (2 < nt) issue_half<D>(t.kbase, t.kv_len, stb, 2, kslot(2), tid);
+  if (1 < nt) issue_half<D>(t.vbase, t.kv_len, stb, 1, vslot(1), tid);
+
+  bf16x8 qf[RBR][KS];
+  f32x4 o[DB][RBR];
+  float m[RBR], l[RBR];
+  bf16x8 pp[NSUB][RBR];  // fp16 P (bits) of each sub-step of the previous tile
+#pragma unroll
+  for (int rb = 0; rb < RBR; ++rb) {
     m[rb] = kNegInf;
     l[rb] = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) pp[sb][rb] = bf16x8{};
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute = [&](const char* stage, int tile) {
-    if (!active) return;
-    const char* Ks = stage;
-    const char* Vs = stage + TILE_BYTES;
-    for (int sub = 0; sub < nsub; ++sub) {
-      const int tsub = tok0 + sub * 32;  // first token of the sub-step in the tile
-      // S^T blocks: lane holds token rows (4 lg + i) of each 16-token block, query row l16.
-      f32x4 s[2][RB];
+  // O^T += V^T P^T over the 32 tokens from `tp` of the (converted) V half `Vs`
+  // with the fp16 P of sub-step `sb`.  A = V^T
+  // rows d = 16 db + l16: two transpose reads, tokens tp + 4 lg + 0..3 and
+  // tp + 16 + 4 lg + 0..3 (the k order of P); source lane s of each 16-lane
+  // group points at token (t0 + s/4), channels 16 db + 4 (s%4) .. +3.
+  auto pv = [&](const char* Vs, int tp, int sb) {
+    const int ta = tp + 4 * lg + (l16 >> 2), tb2 = ta + 16;
+    const int dq = 4 * (l16 & 3);
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int tok = tsub + hb * 16 + l16;
+    for (int db = 0; db < DB; ++db) {
+      const int c = (db * 16 + dq) >> 3, hoff = ((db * 16 + dq) & 7) * 2;
+      const char* pa = Vs + ta * G::ROWB + ((c ^ (ta & (G::CPT - 1))) << 4) + hoff;
+      const char* pb = Vs + tb2 * G::ROWB + ((c ^ (tb2 & (G::CPT - 1))) << 4) + hoff;
+      const bf16x4s x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) bf16x4s*)(pa));
+      const bf16x4s x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) bf16x4s*)(pb));
+      const f16x8 a = __builtin_bit_cast(f16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[hb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int c = ks * 4 + lg;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + tok * G::ROWB + ((c ^ (tok & (G::CPT - 1))) << 4));
-          s[hb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][ks], s[hb][0], 0, 0, 0);
-          if (RBr == 2) s[hb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][ks], s[hb][1], 0, 0, 0);
-        }
-      }
-      // Streaming softmax per row block (base 2), P in the MFMA k order:
-      // slots 0..3 = tokens 4 lg + i of block 0, slots 4..7 of block 1.
-      // m is the reference maximum in scaled units.  It is raised only when a
-      // score exceeds it by more than kLazy (then p <= 2^kLazy, harmless in
-      // float32), so the cross-lane maximum and the rescale of O are skipped
-      // in almost every step.  Full tiles of unmasked nodes skip the
-      // visibility test.
-      const bool full = !t.masked && (tile + 1) * G::TT <= t.kv_len;
-      bf16x8 bp[RB], bq[RB];
-      bp[1] = bf16x8{};
-      bq[1] = bf16x8{};
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if (rb >= RBr) continue;
-        // Scaled scores (base 2); invisible tokens -inf.
-        float v[8];
-        if (full) {
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[hb * 4 + i] = s[hb][rb][i] * p.scale_log2;
-        } else {
-          const uint64_t rmask = t.masked ? row_mask(rb) : ~0ull;
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int tt = tile * G::TT + tsub + hb * 16 + lg * 4 + i;
-              const int bit = t.kv_begin + tt;
-              const bool vis = tt < t.kv_len && (bit >= 64 || ((rmask >> bit) & 1ull));
-              v[hb * 4 + i] = vis ? s[hb][rb][i] * p.scale_log2 : kNegInf;
-            }
-        }
-        float mx = kNegInf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) mx = fmaxf(mx, v[j]);
-        if (__builtin_amdgcn_ballot_w64(mx > m[rb] + kLazy) != 0) {
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float mnew = mx > m[rb] + kLazy ? mx : m[rb];
-          const float alpha = mnew == m[rb] ? 1.f : fast_exp2(m[rb] - mnew);  // 0 when m was -inf
-          m[rb] = mnew;
-          l[rb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) o[db][rb] *= alpha;
-        }
-        const float muse = m[rb] == kNegInf ? 0.f : m[rb];
-        float e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          e[j] = fast_exp2(v[j] - muse);
-          l[rb] += e[j];
-        }
-        // P = hi + lo with hi = bf16(P) and lo = bf16(P - hi).
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          hw[j] = pack_bf16(e[2 * j], e[2 * j + 1]);
-          lw[j] = pack_bf16(e[2 * j] - bf16_lo(hw[j]), e[2 * j + 1] - bf16_hi(hw[j]));
-        }
-        bp[rb] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-        bq[rb] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-      }
-      // O^T += V^T P^T over the 32 tokens.  A = V^T rows d = 16 db + l16: two
-      // transpose reads, tokens tsub + 4 lg + 0..3 and tsub + 16 + 4 lg + 0..3;
-      // source lane s of each 16-lane group points at token (t0 + s/4),
-      // channels 16 db + 4 (s%4) .. +3.
-      const int ta = tsub + 4 * lg + (l16 >> 2), tb2 = ta + 16;
-      const int dq = 4 * (l16 & 3);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int c = (db * 16 + dq) >> 3, hoff = ((db * 16 + dq) & 7) * 2;
-        const char* pa = Vs + ta * G::ROWB + ((c ^ (ta & (G::CPT - 1))) << 4) + hoff;
-        const char* pb = Vs + tb2 * G::ROWB + ((c ^ (tb2 & (G::CPT - 1))) << 4) + hoff;
-        const bf16x4s x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) bf16x4s*)(pa));
-        const bf16x4s x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) bf16x4s*)(pb));
-        const bf16x8 a = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp[0], o[db][0], 0, 0, 0);
-        o[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[0], o[db][0], 0, 0, 0);
-        if (RBr == 2) {
-          o[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp[1], o[db][1], 0, 0, 0);
-          o[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[1], o[db][1], 0, 0, 0);
-        }
-      }
+      for (int rb = 0; rb < RBR; ++rb)
+        o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, pp[sb][rb]), o[db][rb], 0, 0, 0);
     }
   };
 
-  run_tiles<D, 2>(t, stb, tid, compute);
+  // One pipelined step, sub-step `sb` of tile `tile`: S for its 32 tokens
+  // (K half `Ks`), O += P V of the same sub-step of the previous tile (whose
+  // V was waited for and converted at this tile's start) with the P kept
+  // from it, then the softmax of S into pp[sb].  The products of the
+  // previous tile are independent of this step's softmax, so the matrix
+  // cores run them while the vector ALU computes the new P; the
+  // reference-maximum update is branch-free (cross-lane maximum by lane
+  // swaps) so all of it is one basic block, and only the rare rescale of O is
+  // a branch.  Tile 0 has no previous tile (pv_tag false).
+  auto step = [&](auto vis_tag, auto pv_tag, const char* Ks, int tile, int sb) {
+    const int ts = tok0 + sb * 32;
+    constexpr bool kVis = decltype(vis_tag)::value;  // tile needs the visibility test (partial or masked)
+    constexpr bool kPrev = decltype(pv_tag)::value;  // a previous step exists
+    f32x4 s[2][RBR];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int tok = ts + hb * 16 + l16;
+#pragma unroll
+      for (int rb = 0; rb < RBR; ++rb) s[hb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c = ks * 4 + lg;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + tok * G::ROWB + ((c ^ (tok & (G::CPT - 1))) << 4));
+#pragma unroll
+        for (int rb = 0; rb < RBR; ++rb) s[hb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rb][ks], s[hb][rb], 0, 0, 0);
+      }
+    }
+    if constexpr (kPrev) pv(vslot(tile - 1), ts, sb);
+    // Raw scores; lane holds tokens 4 lg + i of each 16-token block, row l16.
+    float x[RBR][8];
+#pragma unroll
+    for (int rb = 0; rb < RBR; ++rb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[rb][j] = s[j >> 2][rb][j & 3];
+    if constexpr (kVis) {
+#pragma unroll
+      for (int rb = 0; rb < RBR; ++rb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int tt = tile * G::TT + ts + (j >> 2) * 16 + lg * 4 + (j & 3);
+          const int bit = t.kv_begin + tt;
+          const bool vis = tt < t.kv_len && (bit >= 64 || ((rmask[rb] >> bit) & 1ull));
+          x[rb][j] = vis ? x[rb][j] : kNegInf;
+        }
+    }
+    // Reference maximum m (scaled units) per row, raised only when the row's
+    // maximum exceeds it by more than kLazy (then p <= 2^kLazy, harmless in
+    // float32): alpha is 1 and O needs no rescale in almost every step.
+    float al[RBR];
+#pragma unroll
+    for (int rb = 0; rb < RBR; ++rb) {
+      float mx = max3(max3(x[rb][0], x[rb][1], x[rb][2]), max3(x[rb][3], x[rb][4], x[rb][5]),
+                      fmaxf(x[rb][6], x[rb][7]));
+      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));  // lanes i, i ^ 32
+      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));  // and i ^ 16: the row
+      const float mr = mx * c2;
+      const float mnew = mr > m[rb] + kLazy ? mr : m[rb];
+      al[rb] = mnew == m[rb] ? 1.f : fast_exp2(m[rb] - mnew);  // 0 when m was -inf
+      m[rb] = mnew;
+      l[rb] *= al[rb];
+    }
+    // P = exp2(x * c - m) in the MFMA k order (slots 0..3: block 0, 4..7: block 1).
+#pragma unroll
+    for (int rb = 0; rb < RBR; ++rb) {
+      const float nm = m[rb] == kNegInf ? 0.f : -m[rb];
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(x[rb][j], c2, nm));
+      uint32_t hw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hw[j] = pack_f16(e[2 * j], e[2 * j + 1]);
+        l[rb] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[j]), __builtin_bit_cast(f16x2, 0x3C003C00u), l[rb],
+                                       false);
+      }
+      pp[sb][rb] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    }
+    // Issue order: the K reads and S products, then the V^T reads and O += P V
+    // products interleaved with the vector work of the softmax.
+    {
+      constexpr int NQK = 2 * KS * RBR;                   // products of S
+      constexpr int NMF = kPrev ? DB * RBR : 1;  // products of O += P V
+      constexpr int NDS = kPrev ? 2 * DB : 0;   // transpose reads
+      constexpr int NVA = RBR * 42;             // softmax vector instructions (approx.)
+      constexpr int VPER = (NVA + NMF - 1) / NMF;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NQK, 0);
+      if (NDS > 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int j = 0; j < NMF; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);
+        if (j + 4 < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    // Keep the new P in this block (the compiler would otherwise sink its
+    // computation next to its use in the following step).
+#pragma unroll
+    for (int rb = 0; rb < RBR; ++rb) asm volatile("" ::"v"(pp[sb][rb]), "v"(l[rb]));
+    bool resc = false;
+#pragma unroll
+    for (int rb = 0; rb < RBR; ++rb) resc = resc || al[rb] != 1.f;
+    if (__builtin_amdgcn_ballot_w64(resc) != 0) {
+      // Everything relative to the old maximum: O (which includes the
+      // products issued above), and the P of the other sub-steps still
+      // waiting for their products.
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rb = 0; rb < RBR; ++rb) o[db][rb] *= al[rb];
+#pragma unroll
+      for (int s2 = 0; s2 < NSUB; ++s2)
+        if (s2 != sb)
+#pragma unroll
+          for (int rb = 0; rb < RBR; ++rb)
+            pp[s2][rb] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(f16x8, pp[s2][rb]) * static_cast<_Float16>(al[rb]));
+    }
+  };
+
+  // Start of iteration i (0 <= i <= nt): wait for group i (K of tile i, V of
+  // tile i - 1), barrier, issue group i + 3 into the halves finished in
+  // iteration i - 1; then either (i = 0) the queries into registers or (i > 0)
+  // the conversion of V of tile i - 1 to fp16, each thread its 32 bytes; a
+  // second barrier publishes them (at i = 0 it frees the query stages, which
+  // group 3 then refills).
+  auto sync = [&](int i) {
+    wait_vmem_n(group_ops(i + 1, nt) + group_ops(i + 2, nt));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS access moves above the barrier
+    // K of tile i - 1 and V of tile i - 2 are finished: refill them at once.
+    // (At i = 0 the refill targets hold the queries: after the reads below.)
+    if (i > 0) {
+      if (i + 3 < nt) issue_half<D>(t.kbase, t.kv_len, stb, i + 3, kslot(i + 3), tid);
+      if (i + 2 < nt) issue_half<D>(t.vbase, t.kv_len, stb, i + 2, vslot(i + 2), tid);
+    }
+    if (i == 0) {
+      if (active) {
+#pragma unroll
+        for (int rb = 0; rb < RBR; ++rb) {
+          const int row = slab * ROWS_W + rb * 16 + l16;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const int c = ks * 4 + lg;
+            const uint4 v = *reinterpret_cast<const uint4*>(qarea + row * G::ROWB + ((c ^ (row & (G::CPT - 1))) << 4));
+            const uint4 z = make_uint4(qok[rb] ? v.x : 0u, qok[rb] ? v.y : 0u, qok[rb] ? v.z : 0u, qok[rb] ? v.w : 0u);
+            qf[rb][ks] = __builtin_bit_cast(bf16x8, z);
+          }
+        }
+      }
+    } else {
+      uint4* vp = reinterpret_cast<uint4*>(vslot(i - 1) + tid * 32);
+      uint4 x0 = vp[0], x1 = vp[1];
+      x0 = make_uint4(bf16x2_to_f16x2_scaled(x0.x), bf16x2_to_f16x2_scaled(x0.y), bf16x2_to_f16x2_scaled(x0.z),
+                      bf16x2_to_f16x2_scaled(x0.w));
+      x1 = make_uint4(bf16x2_to_f16x2_scaled(x1.x), bf16x2_to_f16x2_scaled(x1.y), bf16x2_to_f16x2_scaled(x1.z),
+                      bf16x2_to_f16x2_scaled(x1.w));
+      vp[0] = x0;
+      vp[1] = x1;
+    }
+    wait_lds_all();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (i == 0) {
+      if (3 < nt) issue_half<D>(t.kbase, t.kv_len, stb, 3, kslot(3), tid);
+      if (2 < nt) issue_half<D>(t.vbase, t.kv_len, stb, 2, vslot(2), tid);
+    }
+  };
+  // The NSUB steps of tile i (tile 0: no products of a previous tile).
+  auto tile_steps = [&](auto vis_tag, int i) {
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) step(vis_tag, std::true_type{}, kslot(i), i, sb);
+  };
+  auto tile0_steps = [&](auto vis_tag) {
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) step(vis_tag, std::false_type{}, kslot(0), 0, sb);
+  };
+  if (active && nt > 0) {
+    // Full tiles of unmasked nodes take the branch-free steps; the ragged
+    // last tile, or the one tile of a masked node, the visibility test.  One
+    // straight path per loop keeps the accumulators in place.
+    const int nfull = t.masked ? 0 : t.kv_len / G::TT;
+    sync(0);
+    if (nfull > 0)
+      tile0_steps(std::false_type{});
+    else
+      tile0_steps(std::true_type{});
+    for (int i = 1; i < nfull; ++i) {
+      sync(i);
+      tile_steps(std::false_type{}, i);
+    }
+    for (int i = nfull > 1 ? nfull : 1; i < nt; ++i) {
+      sync(i);
+      tile_steps(std::true_type{}, i);
+    }
+    sync(nt);
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) pv(vslot(nt - 1), tok0 + sb * 32, sb);  // O += P V of the last tile
+  } else {
+    for (int i = 0; i <= nt; ++i) sync(i);
+  }
 
   // Row sums: the four lane groups hold different tokens of the same rows.
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
+  for (int rb = 0; rb < RBR; ++rb) {
     l[rb] += __shfl_xor(l[rb], 16);
     l[rb] += __shfl_xor(l[rb], 32);
   }
   __syncthreads();  // all wavefronts are done with the tiles: reuse the LDS
-  if (TS == 2) {    // uniform across the workgroup
+  if constexpr (TS == 2) {
     // Merge the two token halves of every slab: half 1 hands its state to half 0.
-    float* so = reinterpret_cast<float*>(lds);                // [slab][rb][db][lane][4]
-    float* sml = reinterpret_cast<float*>(lds + kTileBytes);  // [slab][rb][lane][2]
+    float* so = reinterpret_cast<float*>(lds);              // [slab][rb][db][lane][4]
+    float* sml = reinterpret_cast<float*>(lds + kAuxOff);   // [slab][rb][lane][2]
     if (active && half == 1) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if (rb >= RBr) continue;
+      for (int rb = 0; rb < RBR; ++rb) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          *reinterpret_cast<f32x4*>(so + (((slab * RB + rb) * DB + db) * 64 + lane) * 4) = o[db][rb];
-        sml[((slab * RB + rb) * 64 + lane) * 2 + 0] = m[rb];
-        sml[((slab * RB + rb) * 64 + lane) * 2 + 1] = l[rb];
+          *reinterpret_cast<f32x4*>(so + (((slab * RBR + rb) * DB + db) * 64 + lane) * 4) = o[db][rb];
+        sml[((slab * RBR + rb) * 64 + lane) * 2 + 0] = m[rb];
+        sml[((slab * RBR + rb) * 64 + lane) * 2 + 1] = l[rb];
       }
     }
     __syncthreads();
     if (active && half == 0) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if (rb >= RBr) continue;
-        const float m1 = sml[((slab * RB + rb) * 64 + lane) * 2 + 0];
-        const float l1 = sml[((slab * RB + rb) * 64 + lane) * 2 + 1];
+      for (int rb = 0; rb < RBR; ++rb) {
+        const float m1 = sml[((slab * RBR + rb) * 64 + lane) * 2 + 0];
+        const float l1 = sml[((slab * RBR + rb) * 64 + lane) * 2 + 1];
         const float mm = fmaxf(m[rb], m1);
         const float muse = mm == kNegInf ? 0.f : mm;
         const float a0 = fast_exp2(m[rb] - muse), a1 = fast_exp2(m1 - muse);
@@ -434,7 +651,7 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
         m[rb] = mm;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const f32x4 o1 = *reinterpret_cast<const f32x4*>(so + (((slab * RB + rb) * DB + db) * 64 + lane) * 4);
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(so + (((slab * RBR + rb) * DB + db) * 64 + lane) * 4);
           o[db][rb] = o[db][rb] * a0 + o1 * a1;
         }
       }
@@ -442,9 +659,9 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
   }
   if (active && half == 0) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int rb = 0; rb < RBR; ++rb) {
       if (!qok[rb]) continue;
-      const float inv = l[rb] > 0.f ? 1.f / l[rb] : 0.f;
+      const float inv = l[rb] > 0.f ? (1.f / kVScale) / l[rb] : 0.f;  // O carries the 2^-8 of V
       const float lse = l[rb] > 0.f ? (m[rb] + __log2f(l[rb])) * kLn2 : kNegInf;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -514,9 +731,9 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
   const int LPS = 64 / RS;    // lanes per row split
   const int TPI = LPS / LPT;  // tokens per row split per step
   const int nsteps = TPW / TPI;
-  const int tid = threadIdx.x;
+  const int tid = piece_tid();
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int rs = lane / LPS;
   const int tg = (lane % LPS) / LPT, li = lane % LPT;
   const int64_t stb = p.stride_token * static_cast<int64_t>(EB);
@@ -657,7 +874,7 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
   // Merge across wavefronts through LDS: [wave][row][D] numerators, [wave][row] (m, l).
   const int RT = RL * RS;  // rows per wavefront
   float* so = reinterpret_cast<float*>(lds);
-  float* sml = reinterpret_cast<float*>(lds + kTileBytes);
+  float* sml = reinterpret_cast<float*>(lds + kAuxOff);
   __syncthreads();  // every wavefront is done with the tiles
   if (tg == 0) {
 #pragma unroll
@@ -708,7 +925,7 @@ __global__ __launch_bounds__(kPacThreads) void pac_kernel(PacParams p) {
   // The next piece's record travels one dword per lane (lanes 0..11 of every
   // wavefront) while the current piece runs, and is handed over through LDS.
   constexpr int TW = sizeof(DevTask) / 4;
-  uint32_t* const task_lds = reinterpret_cast<uint32_t*>(pac_lds + kTileBytes + kAuxBytes - sizeof(DevTask));
+  uint32_t* const task_lds = reinterpret_cast<uint32_t*>(pac_lds + kAuxOff + kAuxBytes - sizeof(DevTask));
   const int tid = threadIdx.x;
   if (tb < te && tid < TW) task_lds[tid] = reinterpret_cast<const uint32_t*>(p.tasks + tb)[tid];
   __syncthreads();
@@ -717,21 +934,31 @@ __global__ __launch_bounds__(kPacThreads) void pac_kernel(PacParams p) {
     __builtin_memcpy(&task, task_lds, sizeof(DevTask));
     uint32_t next_word = 0;
     if (ti + 1 < te && (tid & 63) < TW) next_word = reinterpret_cast<const uint32_t*>(p.tasks + ti + 1)[tid & 63];
+    // The record is the same in every lane: read it as wave-uniform values so
+    // that everything derived from it (trip counts, active wavefronts) is
+    // scalar control flow and the barriers stay in uniform code.
     TaskInfo t;
-    t.piece = task.piece;
-    t.kv_begin = task.kv_begin;
-    t.kv_len = task.kv_len;
-    t.row_begin = task.row_begin;
-    t.row_count = task.row_count;
-    t.e0 = task.e0;
-    t.masked = (task.flags & kDevMasked) != 0;
-    const int64_t off = (kvh * p.stride_head + task.tok0 * p.stride_token) * esz;
+    t.piece = __builtin_amdgcn_readfirstlane(task.piece);
+    t.kv_begin = __builtin_amdgcn_readfirstlane(task.kv_begin);
+    t.kv_len = __builtin_amdgcn_readfirstlane(task.kv_len);
+    t.row_begin = __builtin_amdgcn_readfirstlane(task.row_begin);
+    t.row_count = __builtin_amdgcn_readfirstlane(task.row_count);
+    t.e0 = __builtin_amdgcn_readfirstlane(task.e0);
+    t.masked = (__builtin_amdgcn_readfirstlane(task.flags) & kDevMasked) != 0;
+    const int64_t tok0 = (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(task.tok0 >> 32))) << 32) |
+                         static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(task.tok0)));
+    const int64_t off = (kvh * p.stride_head + tok0 * p.stride_token) * esz;
     t.kbase = static_cast<const char*>(p.k) + off;
     t.vbase = static_cast<const char*>(p.v) + off;
     bool done = false;
     if constexpr (sizeof(T) == 2) {
       if (t.row_count >= p.mfma_min_rows) {
-        mfma_piece<D>(p, t, kvh);
+        if (t.row_count <= 16)
+          mfma_piece<D, 1, 2>(p, t, kvh);
+        else if (t.row_count <= 128)
+          mfma_piece<D, 2, 2>(p, t, kvh);
+        else
+          mfma_piece<D, 2, 1>(p, t, kvh);
         done = true;
       }
     }

@@ -28,46 +28,69 @@ constexpr int kPorThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
-// Grid: (query, chunk of kPorThreads (head, 4-channel) pairs).
+// Grid: (query, chunk of kPorThreads (head, 4-channel) pairs).  One pass over
+// the chain in batches of kBatch slots: all loads of a batch are in flight
+// together, then the batch is folded into the running (max, sum, O) at the
+// batch maximum (the binary merge applied kBatch times at once).  The slot
+// range is uniform over the workgroup, so the tail batch re-reads a valid
+// slot instead of branching and gives it weight 0.
+constexpr int kBatch = 8;
 template <int D, bool BF16_OUT>
 __global__ __launch_bounds__(kPorThreads) void por_kernel(PorParams p, int chunks) {
   const int r = blockIdx.x / chunks;
   const int chunk = blockIdx.x % chunks;
   const int64_t s0 = p.slot_ptr[r], s1 = p.slot_ptr[r + 1];
   constexpr int C4 = D / 4;
-  {
-    const int idx = chunk * kPorThreads + threadIdx.x;
-    if (idx >= p.hq * C4) return;
-    const int h = idx / C4, c4 = idx % C4;
-    float lmax = kNegInf;
-    for (int64_t s = s0; s < s1; ++s) lmax = fmaxf(lmax, p.lsepart[s * p.hq + h]);
-    const float lref = lmax == kNegInf ? 0.f : lmax;
-    float z = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int64_t s = s0; s < s1; ++s) {
-      const float wgt = __builtin_amdgcn_exp2f((p.lsepart[s * p.hq + h] - lref) * kLog2e);
-      if (wgt == 0.f) continue;  // empty partial: its O may be anything
-      const float4 x = *reinterpret_cast<const float4*>(p.opart + (s * p.hq + h) * D + c4 * 4);
+  const int idx = chunk * kPorThreads + threadIdx.x;
+  if (idx >= p.hq * C4) return;
+  const int h = idx / C4, c4 = idx % C4;
+  float m = kNegInf, z = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t s = s0; s < s1; s += kBatch) {
+    float lse[kBatch];
+    float4 x[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int64_t sj = s + j < s1 ? s + j : s0;
+      lse[j] = s + j < s1 ? p.lsepart[sj * p.hq + h] : kNegInf;
+      x[j] = *reinterpret_cast<const float4*>(p.opart + (sj * p.hq + h) * D + c4 * 4);
+    }
+    float bm = lse[0];
+#pragma unroll
+    for (int j = 1; j < kBatch; ++j) bm = fmaxf(bm, lse[j]);
+    const float mn = fmaxf(m, bm);
+    const float mref = mn == kNegInf ? 0.f : mn;
+    const float a = __builtin_amdgcn_exp2f((m - mref) * kLog2e);  // 0 while m is -inf
+    z *= a;
+    acc.x *= a;
+    acc.y *= a;
+    acc.z *= a;
+    acc.w *= a;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float wgt = __builtin_amdgcn_exp2f((lse[j] - mref) * kLog2e);
+      const bool live = wgt > 0.f;  // an empty partial's O may be anything
       z += wgt;
-      acc.x += wgt * x.x;
-      acc.y += wgt * x.y;
-      acc.z += wgt * x.z;
-      acc.w += wgt * x.w;
+      acc.x += live ? wgt * x[j].x : 0.f;
+      acc.y += live ? wgt * x[j].y : 0.f;
+      acc.z += live ? wgt * x[j].z : 0.f;
+      acc.w += live ? wgt * x[j].w : 0.f;
     }
-    const float inv = z > 0.f ? 1.f / z : 0.f;
-    const int64_t o = (static_cast<int64_t>(r) * p.hq + h) * D + c4 * 4;
-    if (BF16_OUT) {
-      f32x2 a = {acc.x * inv, acc.y * inv}, b = {acc.z * inv, acc.w * inv};
-      uint2 u;
-      u.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2n));
-      u.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2n));
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = u;
-    } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) =
-          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    }
-    if (p.lse_out && c4 == 0) p.lse_out[static_cast<int64_t>(r) * p.hq + h] = z > 0.f ? lref + __logf(z) : kNegInf;
+    m = mn;
   }
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  const int64_t o = (static_cast<int64_t>(r) * p.hq + h) * D + c4 * 4;
+  if (BF16_OUT) {
+    f32x2 a = {acc.x * inv, acc.y * inv}, b = {acc.z * inv, acc.w * inv};
+    uint2 u;
+    u.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2n));
+    u.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2n));
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = u;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
+  if (p.lse_out && c4 == 0) p.lse_out[static_cast<int64_t>(r) * p.hq + h] = z > 0.f ? m + __logf(z) : kNegInf;
 }
 
 // Overwrite a buffer with 128-bit stores (evicts L2 and the last-level cache).

@@ -115,6 +115,7 @@ struct PacParams {
   const int32_t* entry_slot;
   int64_t stride_head;   // elements
   int64_t stride_token;  // elements
+  int64_t q_bytes;       // bytes of q ([B][hq][d]); below 2^31 (32-bit gather offsets)
   int32_t num_bins;
   int32_t hq;
   int32_t hkv;

@@ -122,6 +122,16 @@ def test_row_counts_single_node(rows):
     check(spec, t, out, lse)
 
 
+@pytest.mark.parametrize("rows", [3, 16, 40, 64, 100, 128, 200, 256])
+def test_row_counts_head_dim_64(rows):
+    """Head dim 64: 128-token tiles, so every wavefront runs several 32-token sub-steps per tile."""
+    spec = workloads.TreeSpec(f"rows{rows}-d64", np.array([-1]), np.array([1000]), np.array([0]), np.array([0]),
+                              rows, 1, 64, "bf16", 79)
+    say(f"rows {rows} at head dim 64")
+    t, plan, out, lse = run(spec, num_bins=5)
+    check(spec, t, out, lse)
+
+
 @pytest.mark.parametrize("rows", [1, 2, 4, 8, 12, 15])
 def test_row_counts_dot_path(rows):
     """The wavefront dot-product path for bf16 pieces below 16 rows (PST_PLAN_DOT_SMALL)."""
