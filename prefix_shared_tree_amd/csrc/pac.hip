@@ -58,7 +58,10 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-constexpr int NW = kPacThreads / 64;  // wavefronts per workgroup
+// Wavefronts per workgroup: two per SIMD, so that one wavefront's matrix-core
+// work overlaps the other's vector work.
+template <typename T>
+constexpr int kWaves = 8;
 constexpr int NSTAGE = 4;             // LDS tile stages
 constexpr int TILE_BYTES = 16384;     // bytes of one K (or V) tile
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
@@ -136,16 +139,33 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
 }
 
-// Wait until at most n of this wavefront's vector memory operations are
-// outstanding (n in {0, 4, 8}); expcnt and lgkmcnt are left alone.
-__device__ __forceinline__ void wait_vmem(int n) {
-  if (n >= 8)
-    __builtin_amdgcn_s_waitcnt(0x0F78);
-  else if (n >= 4)
-    __builtin_amdgcn_s_waitcnt(0x0F74);
-  else
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+// Wait until at most n (0..16) of this wavefront's vector memory operations
+// are outstanding; expcnt and lgkmcnt are left alone (vmcnt: bits 3:0 and
+// 15:14 of the s_waitcnt immediate).
+#define PST_VMCNT(n) (0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+__device__ __forceinline__ void wait_vmem_n(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(PST_VMCNT(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(PST_VMCNT(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(PST_VMCNT(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(PST_VMCNT(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(PST_VMCNT(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(PST_VMCNT(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(PST_VMCNT(6)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(PST_VMCNT(7)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(PST_VMCNT(8)); break;
+    case 9: __builtin_amdgcn_s_waitcnt(PST_VMCNT(9)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(PST_VMCNT(10)); break;
+    case 11: __builtin_amdgcn_s_waitcnt(PST_VMCNT(11)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(PST_VMCNT(12)); break;
+    case 13: __builtin_amdgcn_s_waitcnt(PST_VMCNT(13)); break;
+    case 14: __builtin_amdgcn_s_waitcnt(PST_VMCNT(14)); break;
+    case 15: __builtin_amdgcn_s_waitcnt(PST_VMCNT(15)); break;
+    default: __builtin_amdgcn_s_waitcnt(PST_VMCNT(16)); break;
+  }
 }
+#undef PST_VMCNT
+__device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -195,10 +215,13 @@ __device__ __forceinline__ void write_partial(const PacParams& p, const TaskInfo
   if (write_lse) p.lsepart[slot * p.hq + head] = lse;
 }
 
-// DMA of tile `tile` of the piece into stage `stage`: every wavefront writes
-// two 1 KB blocks of K and two of V; lane L of a block fills 16-byte chunk
-// position P = block*64 + L, i.e. token P / CPT, chunk (P % CPT) ^ (token % CPT).
-template <int D, int EB>
+// DMA of tile `tile` of the piece into stage `stage`: the 16 1 KB blocks of
+// K and of V are spread over the NW wavefronts; lane L of a block fills
+// 16-byte chunk position P = block*64 + L, i.e. token P / CPT, chunk
+// (P % CPT) ^ (token % CPT).
+template <int NW>
+constexpr int kHalfOps = TILE_BYTES / 1024 / NW;  // DMA operations per thread for one K (or V) tile
+template <int D, int EB, int NW>
 __device__ __forceinline__ void issue_tile(const TaskInfo& t, int64_t stb, int tile, int stage, int tid) {
   using G = Geo<D, EB>;
   const int tok_base = tile * G::TT;
@@ -208,7 +231,7 @@ __device__ __forceinline__ void issue_tile(const TaskInfo& t, int64_t stb, int t
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   char* st = pac_lds + stage * STAGE_BYTES;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < kHalfOps<NW>; ++c) {
     const int b = c * NW + w;
     const int P = b * 64 + lane;
     const int tok = P / G::CPT, phys = P % G::CPT;
@@ -219,27 +242,27 @@ __device__ __forceinline__ void issue_tile(const TaskInfo& t, int64_t stb, int t
 }
 
 // Tiles 0 .. NSTAGE-2 (issued before the queries are gathered).
-template <int D, int EB>
+template <int D, int EB, int NW>
 __device__ __forceinline__ void issue_prologue(const TaskInfo& t, int64_t stb, int tid) {
   using G = Geo<D, EB>;
   const int ntiles = (t.kv_len + G::TT - 1) / G::TT;
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i)
-    if (i < ntiles) issue_tile<D, EB>(t, stb, i, i, tid);
+    if (i < ntiles) issue_tile<D, EB, NW>(t, stb, i, i, tid);
 }
 
-// The tile loop: wait for tile i (4 DMA operations per thread and tile), a
+// The tile loop: wait for tile i (2 kHalfOps DMA operations per thread and tile), a
 // barrier without a memory fence (which would drain every DMA in flight),
 // refill the stage of tile i-1 with tile i+3, compute tile i.
-template <int D, int EB, typename F>
+template <int D, int EB, int NW, typename F>
 __device__ __forceinline__ void run_tiles(const TaskInfo& t, int64_t stb, int tid, F&& compute) {
   using G = Geo<D, EB>;
   const int ntiles = (t.kv_len + G::TT - 1) / G::TT;
   for (int tile = 0; tile < ntiles; ++tile) {
-    wait_vmem(4 * min(NSTAGE - 2, ntiles - 1 - tile));
+    wait_vmem_n(2 * kHalfOps<NW> * min(NSTAGE - 2, ntiles - 1 - tile));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");  // no LDS access moves above the barrier
-    if (tile + NSTAGE - 1 < ntiles) issue_tile<D, EB>(t, stb, tile + NSTAGE - 1, (tile + NSTAGE - 1) % NSTAGE, tid);
+    if (tile + NSTAGE - 1 < ntiles) issue_tile<D, EB, NW>(t, stb, tile + NSTAGE - 1, (tile + NSTAGE - 1) % NSTAGE, tid);
     compute(pac_lds + (tile % NSTAGE) * STAGE_BYTES, tile);
   }
 }
@@ -268,9 +291,9 @@ __device__ __forceinline__ char* kslot(int j) { return pac_lds + (j % NSTAGE) * 
 __device__ __forceinline__ char* vslot(int j) { return pac_lds + (j % NSTAGE) * STAGE_BYTES + TILE_BYTES; }
 
 // DMA of the K (or V) half of tile `tile` (16 KB) into `dst`: every wavefront
-// writes two 1 KB blocks; lane L of block b fills chunk position P = 64 b + L,
-// i.e. token P / CPT, chunk (P % CPT) ^ (token % CPT).
-template <int D>
+// writes kHalfOps 1 KB blocks; lane L of block b fills chunk position
+// P = 64 b + L, i.e. token P / CPT, chunk (P % CPT) ^ (token % CPT).
+template <int D, int NW>
 __device__ __forceinline__ void issue_half(const char* base, int kv_len, int64_t stb, int tile, char* dst, int tid) {
   using G = Geo<D, 2>;
   const int tok_base = tile * G::TT;
@@ -278,7 +301,7 @@ __device__ __forceinline__ void issue_half(const char* base, int kv_len, int64_t
   const __amdgpu_buffer_rsrc_t r = make_rsrc(base + tok_base * stb, bytes);
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < kHalfOps<NW>; ++c) {
     const int b = c * NW + w;
     const int P = b * 64 + lane;
     const int tok = P / G::CPT, phys = P % G::CPT;
@@ -287,28 +310,16 @@ __device__ __forceinline__ void issue_half(const char* base, int kv_len, int64_t
 }
 
 // DMA schedule of a piece of nt tiles: group j holds K of tile j (j < nt)
-// and V of tile j - 1 (1 <= j <= nt), two operations per thread each.
+// and V of tile j - 1 (1 <= j <= nt), kHalfOps operations per thread each.
 // Iteration i of the tile loop consumes group i (QK of tile i, PV of tile
 // i - 1) and issues group i + 3, so three groups stay in flight; K of tile
 // i + 3 refills the K half of tile i - 1 and V of tile i + 2 the V half of
 // tile i - 2, both finished before iteration i's barrier.
-__device__ __forceinline__ int group_ops(int j, int nt) { return (j < nt ? 2 : 0) + (j >= 1 && j <= nt ? 2 : 0); }
-
-// Wait until at most n (0..8) of this wavefront's vector memory operations are outstanding.
-__device__ __forceinline__ void wait_vmem_n(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-  }
+template <int NW>
+__device__ __forceinline__ int group_ops(int j, int nt) {
+  return (j < nt ? kHalfOps<NW> : 0) + (j >= 1 && j <= nt ? kHalfOps<NW> : 0);
 }
-__device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
+
 
 // Each wavefront owns RBR blocks of 16 rows of a slab; TS wavefronts share a
 // slab, each taking TT/TS tokens of every tile in NSUB = TT/(32 TS) sub-steps
@@ -316,13 +327,14 @@ __device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC0
 // sub-steps are software-pipelined: step k computes S = K Q^T and the
 // softmax of step k while the matrix cores run O += P V of step k - 1, so
 // matrix-core and vector work overlap inside a wavefront.
-template <int D, int RBR, int TS>
+template <int D, int RBR, int TS, int NW>
 __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t, int kvh) {
   using G = Geo<D, 2>;
   constexpr int KS = D / 32;  // k-steps of S^T = K Q^T
   constexpr int DB = D / 16;  // d-blocks of O^T
   constexpr int NSUB = G::TT / (32 * TS);  // 32-token sub-steps per wavefront and tile
   constexpr int ROWS_W = 16 * RBR;
+  constexpr bool kSpread = TS == 1;  // refills issued inside the steps (see `step`)
   constexpr int QOPS = kMaxRows * G::CPT / 64 / NW;  // Q DMA operations per thread at most
   char* const lds = pac_lds;
   const int tid = piece_tid();
@@ -372,11 +384,11 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     for (int o = 0; o < QOPS; ++o)
       if (o * NW + w < qops_total) dma16(rq, static_cast<int>(qoff[o]), lds_addr(qarea + (o * NW + w) * 1024));
   }
-  if (0 < nt) issue_half<D>(t.kbase, t.kv_len, stb, 0, kslot(0), tid);
-  if (1 < nt) issue_half<D>(t.kbase, t.kv_len, stb, 1, kslot(1), tid);
-  if (0 < nt) issue_half<D>(t.vbase, t.kv_len, stb, 0, vslot(0), tid);
-  if (2 < nt) issue_half<D>(t.kbase, t.kv_len, stb, 2, kslot(2), tid);
-  if (1 < nt) issue_half<D>(t.vbase, t.kv_len, stb, 1, vslot(1), tid);
+  if (0 < nt) issue_half<D, NW>(t.kbase, t.kv_len, stb, 0, kslot(0), tid);
+  if (1 < nt) issue_half<D, NW>(t.kbase, t.kv_len, stb, 1, kslot(1), tid);
+  if (0 < nt) issue_half<D, NW>(t.vbase, t.kv_len, stb, 0, vslot(0), tid);
+  if (2 < nt) issue_half<D, NW>(t.kbase, t.kv_len, stb, 2, kslot(2), tid);
+  if (1 < nt) issue_half<D, NW>(t.vbase, t.kv_len, stb, 1, vslot(1), tid);
 
   bf16x8 qf[RBR][KS];
   f32x4 o[DB][RBR];
@@ -441,7 +453,18 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
         for (int rb = 0; rb < RBR; ++rb) s[hb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rb][ks], s[hb][rb], 0, 0, 0);
       }
     }
-    if constexpr (kPrev) pv(vslot(tile - 1), ts, sb);
+    if constexpr (kPrev) {
+      // Compute-bound layout (TS = 1): this wavefront's share of the refills
+      // of iteration `tile` (K of tile + 3 in the first sub-step, V of tile +
+      // 2 in the last), issued here rather than all at once after the
+      // barrier: a DMA instruction holds its wavefront for tens of cycles,
+      // and eight wavefronts issuing together right after a barrier queue up
+      // behind each other.  (Bandwidth-bound layouts refill at the barrier,
+      // as early as possible.)
+      if (kSpread && sb == 0 && tile + 3 < nt) issue_half<D, NW>(t.kbase, t.kv_len, stb, tile + 3, kslot(tile + 3), tid);
+      if (kSpread && sb == NSUB - 1 && tile + 2 < nt) issue_half<D, NW>(t.vbase, t.kv_len, stb, tile + 2, vslot(tile + 2), tid);
+      pv(vslot(tile - 1), ts, sb);
+    }
     // Raw scores; lane holds tokens 4 lg + i of each 16-token block, row l16.
     float x[RBR][8];
 #pragma unroll
@@ -538,18 +561,19 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
   // Start of iteration i (0 <= i <= nt): wait for group i (K of tile i, V of
   // tile i - 1), barrier, issue group i + 3 into the halves finished in
   // iteration i - 1; then either (i = 0) the queries into registers or (i > 0)
-  // the conversion of V of tile i - 1 to fp16, each thread its 32 bytes; a
+  // the conversion of V of tile i - 1 to fp16, each thread its share; a
   // second barrier publishes them (at i = 0 it frees the query stages, which
   // group 3 then refills).
-  auto sync = [&](int i) {
-    wait_vmem_n(group_ops(i + 1, nt) + group_ops(i + 2, nt));
+  auto sync = [&](int i, bool refill) {
+    wait_vmem_n(group_ops<NW>(i + 1, nt) + group_ops<NW>(i + 2, nt));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");  // no LDS access moves above the barrier
-    // K of tile i - 1 and V of tile i - 2 are finished: refill them at once.
-    // (At i = 0 the refill targets hold the queries: after the reads below.)
-    if (i > 0) {
-      if (i + 3 < nt) issue_half<D>(t.kbase, t.kv_len, stb, i + 3, kslot(i + 3), tid);
-      if (i + 2 < nt) issue_half<D>(t.vbase, t.kv_len, stb, i + 2, vslot(i + 2), tid);
+    // K of tile i - 1 and V of tile i - 2 are finished: refill them (here, or
+    // in the steps of tile i when `refill` is false; at i = 0 the refill
+    // targets hold the queries: after the reads below).
+    if (i > 0 && refill) {
+      if (i + 3 < nt) issue_half<D, NW>(t.kbase, t.kv_len, stb, i + 3, kslot(i + 3), tid);
+      if (i + 2 < nt) issue_half<D, NW>(t.vbase, t.kv_len, stb, i + 2, vslot(i + 2), tid);
     }
     if (i == 0) {
       if (active) {
@@ -566,21 +590,22 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
         }
       }
     } else {
-      uint4* vp = reinterpret_cast<uint4*>(vslot(i - 1) + tid * 32);
-      uint4 x0 = vp[0], x1 = vp[1];
-      x0 = make_uint4(bf16x2_to_f16x2_scaled(x0.x), bf16x2_to_f16x2_scaled(x0.y), bf16x2_to_f16x2_scaled(x0.z),
-                      bf16x2_to_f16x2_scaled(x0.w));
-      x1 = make_uint4(bf16x2_to_f16x2_scaled(x1.x), bf16x2_to_f16x2_scaled(x1.y), bf16x2_to_f16x2_scaled(x1.z),
-                      bf16x2_to_f16x2_scaled(x1.w));
-      vp[0] = x0;
-      vp[1] = x1;
+      constexpr int CV = TILE_BYTES / (NW * 64) / 16;  // 16-byte chunks per thread
+      uint4* vp = reinterpret_cast<uint4*>(vslot(i - 1) + tid * CV * 16);
+      uint4 x[CV];
+#pragma unroll
+      for (int c = 0; c < CV; ++c) x[c] = vp[c];
+#pragma unroll
+      for (int c = 0; c < CV; ++c)
+        vp[c] = make_uint4(bf16x2_to_f16x2_scaled(x[c].x), bf16x2_to_f16x2_scaled(x[c].y),
+                           bf16x2_to_f16x2_scaled(x[c].z), bf16x2_to_f16x2_scaled(x[c].w));
     }
     wait_lds_all();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (i == 0) {
-      if (3 < nt) issue_half<D>(t.kbase, t.kv_len, stb, 3, kslot(3), tid);
-      if (2 < nt) issue_half<D>(t.vbase, t.kv_len, stb, 2, vslot(2), tid);
+      if (3 < nt) issue_half<D, NW>(t.kbase, t.kv_len, stb, 3, kslot(3), tid);
+      if (2 < nt) issue_half<D, NW>(t.vbase, t.kv_len, stb, 2, vslot(2), tid);
     }
   };
   // The NSUB steps of tile i (tile 0: no products of a previous tile).
@@ -597,24 +622,24 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     // last tile, or the one tile of a masked node, the visibility test.  One
     // straight path per loop keeps the accumulators in place.
     const int nfull = t.masked ? 0 : t.kv_len / G::TT;
-    sync(0);
+    sync(0, !kSpread);
     if (nfull > 0)
       tile0_steps(std::false_type{});
     else
       tile0_steps(std::true_type{});
     for (int i = 1; i < nfull; ++i) {
-      sync(i);
+      sync(i, !kSpread);
       tile_steps(std::false_type{}, i);
     }
     for (int i = nfull > 1 ? nfull : 1; i < nt; ++i) {
-      sync(i);
+      sync(i, !kSpread);
       tile_steps(std::true_type{}, i);
     }
-    sync(nt);
+    sync(nt, true);
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) pv(vslot(nt - 1), tok0 + sb * 32, sb);  // O += P V of the last tile
   } else {
-    for (int i = 0; i <= nt; ++i) sync(i);
+    for (int i = 0; i <= nt; ++i) sync(i, true);
   }
 
   // Row sums: the four lane groups hold different tokens of the same rows.
@@ -717,7 +742,7 @@ struct Elem<uint16_t> {  // bfloat16 bits
 // Up to RL = 8 rows per lane; RS row splits (2 when the piece has more than 8
 // rows): lanes [k*64/RS, (k+1)*64/RS) own rows [k*RL, (k+1)*RL) and read the
 // same tokens.  Each wavefront takes TT/8 tokens of every tile, TPI at a time.
-template <typename T, int D>
+template <typename T, int D, int NW>
 __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t, int kvh) {
   constexpr int EB = sizeof(T);
   using G = Geo<D, EB>;
@@ -740,7 +765,7 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
   const int R = t.row_count;
   const int r0 = rs * RL;
 
-  issue_prologue<D, EB>(t, stb, tid);
+  issue_prologue<D, EB, NW>(t, stb, tid);
 
   // Branch-free gather (dead rows read row 0 of the task and are zeroed).
   uint32_t q[RL][4];
@@ -761,18 +786,19 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
     q[r][2] = qok[r] ? u.z : 0u;
     q[r][3] = qok[r] ? u.w : 0u;
   }
-  // The row this thread writes at the end (one (row, 4 channels) per thread).
+  // The (row, 4 channels) chunks this thread writes at the end: chunk
+  // tid + k * threads.
   constexpr int C4 = D / 4;
-  static_assert(kMaxRowsDot * C4 <= kPacThreads, "one output chunk per thread");
-  const int out_r = tid / C4, out_c4 = tid % C4;
-  int out_slot = 0, out_head = 0;
-  {
+  constexpr int OUTS = (kMaxRowsDot * C4 + NW * 64 - 1) / (NW * 64);
+  int out_slot[OUTS], out_head[OUTS];
+#pragma unroll
+  for (int k = 0; k < OUTS; ++k) {
     int entry = t.e0 + t.row_begin / p.g, head = kvh * p.g + t.row_begin % p.g;
-    row_target(p, t, kvh, out_r, &entry, &head);
-    out_slot = p.entry_slot[entry];
-    out_head = head;
+    row_target(p, t, kvh, (tid + k * NW * 64) / C4, &entry, &head);
+    out_slot[k] = p.entry_slot[entry];
+    out_head[k] = head;
   }
-  wait_vmem(0);  // queries in registers before the tile loop (see the matrix-core path)
+  wait_vmem_n(0);  // queries in registers before the tile loop (see the matrix-core path)
   const int nr = min(RL, max(0, R - r0));  // live rows of this lane (uniform per row split)
   float o[RL][E];
   float m[RL], l[RL];
@@ -849,7 +875,7 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
     }
   };
 
-  run_tiles<D, EB>(t, stb, tid, compute);
+  run_tiles<D, EB, NW>(t, stb, tid, compute);
 
   // Merge the TPI token streams of this row split (lanes li, li + LPT, ...).
   for (int off = LPT; off < LPS; off <<= 1) {
@@ -892,8 +918,10 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
   }
   __syncthreads();
   // Thread -> (row, 4 channels).
-  if (out_r < R) {
-    const int r = out_r, c4 = out_c4;
+#pragma unroll
+  for (int k = 0; k < OUTS; ++k) {
+    const int r = (tid + k * NW * 64) / C4, c4 = (tid + k * NW * 64) % C4;
+    if (r >= R) break;
     float mm = kNegInf;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) mm = fmaxf(mm, sml[(ww * RT + r) * 2]);
@@ -912,12 +940,14 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse = lt > 0.f ? (mm + __log2f(lt)) * kLn2 : kNegInf;
     const float v4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-    write_partial(p, t, out_slot, out_head, D, c4 * 4, v4, lse, c4 == 0);
+    write_partial(p, t, out_slot[k], out_head[k], D, c4 * 4, v4, lse, c4 == 0);
   }
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kPacThreads) void pac_kernel(PacParams p) {
+__global__ __launch_bounds__(kWaves<T> * 64) __attribute__((amdgpu_waves_per_eu(kWaves<T> / 4, kWaves<T> / 4)))
+void pac_kernel(PacParams p) {
+  constexpr int NW = kWaves<T>;
   const int bin = blockIdx.x % p.num_bins;
   const int kvh = blockIdx.x / p.num_bins;
   const int tb = p.bin_ptr[bin], te = p.bin_ptr[bin + 1];
@@ -953,16 +983,18 @@ __global__ __launch_bounds__(kPacThreads) void pac_kernel(PacParams p) {
     bool done = false;
     if constexpr (sizeof(T) == 2) {
       if (t.row_count >= p.mfma_min_rows) {
+        // Slabs of 16 RBR rows, TS wavefronts per slab.
+        static_assert(NW == 8, "row dispatch for 8 wavefronts");
         if (t.row_count <= 16)
-          mfma_piece<D, 1, 2>(p, t, kvh);
+          mfma_piece<D, 1, 2, NW>(p, t, kvh);
         else if (t.row_count <= 128)
-          mfma_piece<D, 2, 2>(p, t, kvh);
+          mfma_piece<D, 2, 2, NW>(p, t, kvh);
         else
-          mfma_piece<D, 2, 1>(p, t, kvh);
+          mfma_piece<D, 2, 1, NW>(p, t, kvh);
         done = true;
       }
     }
-    if (!done) dot_piece<T, D>(p, t, kvh);
+    if (!done) dot_piece<T, D, NW>(p, t, kvh);
     __syncthreads();  // the piece is finished with the LDS (and with task_lds)
     if (tid < TW) task_lds[tid] = next_word;
     __syncthreads();
@@ -979,7 +1011,7 @@ int launch_one(const PacParams& p, void* stream) {
     if (e != hipSuccess) return static_cast<int>(e);
     configured = true;
   }
-  hipLaunchKernelGGL((pac_kernel<T, D>), dim3(grid), dim3(kPacThreads), kLdsBytes, static_cast<hipStream_t>(stream),
+  hipLaunchKernelGGL((pac_kernel<T, D>), dim3(grid), dim3(kWaves<T> * 64), kLdsBytes, static_cast<hipStream_t>(stream),
                      p);
   return static_cast<int>(hipGetLastError());
 }
@@ -997,13 +1029,13 @@ int launch_pac(const PacParams& p, int in_dtype, int head_dim, void* stream) {
 int pac_blocks_per_cu(int in_dtype, int head_dim, int* blocks) {
   hipError_t e;
   if (in_dtype == PST_BF16 && head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 128>, kPacThreads, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 128>, kWaves<uint16_t> * 64, kLdsBytes);
   else if (in_dtype == PST_BF16)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 64>, kPacThreads, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 64>, kWaves<uint16_t> * 64, kLdsBytes);
   else if (head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 128>, kPacThreads, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 128>, kWaves<float> * 64, kLdsBytes);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 64>, kPacThreads, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 64>, kWaves<float> * 64, kLdsBytes);
   return static_cast<int>(e);
 }
 

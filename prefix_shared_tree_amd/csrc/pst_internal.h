@@ -15,10 +15,9 @@ constexpr uint32_t kPlanMagic = 0x32545350u;  // "PST2"
 constexpr uint32_t kCostMagic = 0x33545350u;  // "PST3"
 
 constexpr int kTile = 64;         // tokens per K/V tile of the partial-attention kernel
-constexpr int kMaxRows = 256;     // rows one workgroup holds (MFMA path: 8 waves x 32 rows)
+constexpr int kMaxRows = 256;     // rows one workgroup holds (matrix-core path: 8 waves x 32 rows)
 constexpr int kMfmaMinRowsDot = 16;  // matrix-core threshold with PST_PLAN_DOT_SMALL (else 1)
 constexpr int kMaxRowsDot = 16;   // the dot-product path keeps up to this many rows in registers
-constexpr int kPacThreads = 512;  // 8 wavefronts of 64
 
 void set_error(const std::string& msg);
 
