@@ -393,11 +393,16 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
   bf16x8 qf[RBR][KS];
   f32x4 o[DB][RBR];
   float m[RBR], l[RBR];
+  float nm[RBR];   // -m, or 0 while m is -inf (the exponent offset of P)
+  float thr[RBR];  // (m + kLazy) / c: raw scores above it raise the reference maximum
   bf16x8 pp[NSUB][RBR];  // fp16 P (bits) of each sub-step of the previous tile
+  const float ic2 = 1.f / c2;
 #pragma unroll
   for (int rb = 0; rb < RBR; ++rb) {
     m[rb] = kNegInf;
     l[rb] = 0.f;
+    nm[rb] = 0.f;
+    thr[rb] = kNegInf;
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) pp[sb][rb] = bf16x8{};
 #pragma unroll
@@ -426,15 +431,35 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     }
   };
 
+  // Raise row rb's reference maximum to this lane group's maximum mx (raw
+  // score units) when it exceeds m + kLazy; *al = the factor that takes
+  // values relative to the old reference to the new one.
+  auto update_ref = [&](int rb, float mx, float* al) {
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));  // lanes i, i ^ 32
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));  // and i ^ 16: the row
+    const float mr = mx * c2;
+    const float mnew = mr > m[rb] + kLazy ? mr : m[rb];
+    *al = mnew == m[rb] ? 1.f : fast_exp2(m[rb] - mnew);  // 0 when m was -inf
+    m[rb] = mnew;
+    l[rb] *= *al;
+    nm[rb] = mnew == kNegInf ? 0.f : -mnew;
+    thr[rb] = mnew == kNegInf ? kNegInf : (mnew + kLazy) * ic2;
+  };
+
   // One pipelined step, sub-step `sb` of tile `tile`: S for its 32 tokens
   // (K half `Ks`), O += P V of the same sub-step of the previous tile (whose
   // V was waited for and converted at this tile's start) with the P kept
   // from it, then the softmax of S into pp[sb].  The products of the
   // previous tile are independent of this step's softmax, so the matrix
-  // cores run them while the vector ALU computes the new P; the
-  // reference-maximum update is branch-free (cross-lane maximum by lane
-  // swaps) so all of it is one basic block, and only the rare rescale of O is
-  // a branch.  Tile 0 has no previous tile (pv_tag false).
+  // cores run them while the vector ALU computes the new P.  With two
+  // wavefronts per slab the reference-maximum update is branch-free
+  // (cross-lane maximum by lane swaps), so all of it is one basic block; with
+  // one slab per wavefront (compute-bound) a per-lane test skips the
+  // cross-lane maximum in almost every step and the products follow it.
+  // Only the rare rescale of O is a branch.  Tile 0 has no previous tile
+  // (pv_tag false).
   auto step = [&](auto vis_tag, auto pv_tag, const char* Ks, int tile, int sb) {
     const int ts = tok0 + sb * 32;
     constexpr bool kVis = decltype(vis_tag)::value;  // tile needs the visibility test (partial or masked)
@@ -463,7 +488,7 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
       // as early as possible.)
       if (kSpread && sb == 0 && tile + 3 < nt) issue_half<D, NW>(t.kbase, t.kv_len, stb, tile + 3, kslot(tile + 3), tid);
       if (kSpread && sb == NSUB - 1 && tile + 2 < nt) issue_half<D, NW>(t.vbase, t.kv_len, stb, tile + 2, vslot(tile + 2), tid);
-      pv(vslot(tile - 1), ts, sb);
+      if constexpr (!kSpread) pv(vslot(tile - 1), ts, sb);
     }
     // Raw scores; lane holds tokens 4 lg + i of each 16-token block, row l16.
     float x[RBR][8];
@@ -484,29 +509,49 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     }
     // Reference maximum m (scaled units) per row, raised only when the row's
     // maximum exceeds it by more than kLazy (then p <= 2^kLazy, harmless in
-    // float32): alpha is 1 and O needs no rescale in almost every step.
+    // fp16 and float32): alpha is 1 and O needs no rescale in almost every
+    // step.
     float al[RBR];
+    bool resc = false;
+    if constexpr (kSpread) {
+      // One slab per wavefront (compute-bound): each lane tests its own
+      // scores against the raw threshold; only when one exceeds it does the
+      // wavefront form the row maxima across the four lanes of a row (lane
+      // swaps) and move the references.
+      bool up = false;
 #pragma unroll
-    for (int rb = 0; rb < RBR; ++rb) {
-      float mx = max3(max3(x[rb][0], x[rb][1], x[rb][2]), max3(x[rb][3], x[rb][4], x[rb][5]),
-                      fmaxf(x[rb][6], x[rb][7]));
-      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));  // lanes i, i ^ 32
-      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));  // and i ^ 16: the row
-      const float mr = mx * c2;
-      const float mnew = mr > m[rb] + kLazy ? mr : m[rb];
-      al[rb] = mnew == m[rb] ? 1.f : fast_exp2(m[rb] - mnew);  // 0 when m was -inf
-      m[rb] = mnew;
-      l[rb] *= al[rb];
+      for (int rb = 0; rb < RBR; ++rb) {
+        const float mx = max3(max3(x[rb][0], x[rb][1], x[rb][2]), max3(x[rb][3], x[rb][4], x[rb][5]),
+                              fmaxf(x[rb][6], x[rb][7]));
+        up = up || mx > thr[rb];
+        al[rb] = mx;  // the lane maximum, until the update below
+      }
+      resc = __builtin_amdgcn_ballot_w64(up) != 0;
+      if (resc) {
+#pragma unroll
+        for (int rb = 0; rb < RBR; ++rb) update_ref(rb, al[rb], &al[rb]);
+      }
+      // O += P V of the same sub-step of the previous tile (P relative to the
+      // old references: rescaled with O below), issued between the vector
+      // work of the new P.
+      if constexpr (kPrev) pv(vslot(tile - 1), ts, sb);
+    } else {
+      // Branch-free (the products of O += P V above overlap it): every step
+      // forms the row maxima.
+#pragma unroll
+      for (int rb = 0; rb < RBR; ++rb) {
+        const float mx = max3(max3(x[rb][0], x[rb][1], x[rb][2]), max3(x[rb][3], x[rb][4], x[rb][5]),
+                              fmaxf(x[rb][6], x[rb][7]));
+        update_ref(rb, mx, &al[rb]);
+        resc = resc || al[rb] != 1.f;
+      }
     }
     // P = exp2(x * c - m) in the MFMA k order (slots 0..3: block 0, 4..7: block 1).
 #pragma unroll
     for (int rb = 0; rb < RBR; ++rb) {
-      const float nm = m[rb] == kNegInf ? 0.f : -m[rb];
       float e[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(x[rb][j], c2, nm));
+      for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(x[rb][j], c2, nm[rb]));
       uint32_t hw[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -516,16 +561,19 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
       }
       pp[sb][rb] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
     }
-    // Issue order: the K reads and S products, then the V^T reads and O += P V
-    // products interleaved with the vector work of the softmax.
+    // Issue order: (branch-free layout: the K reads and S products, then) the
+    // V^T reads and O += P V products interleaved with the vector work of the
+    // softmax.
     {
-      constexpr int NQK = 2 * KS * RBR;                   // products of S
+      constexpr int NQK = 2 * KS * RBR;          // products of S
       constexpr int NMF = kPrev ? DB * RBR : 1;  // products of O += P V
       constexpr int NDS = kPrev ? 2 * DB : 0;   // transpose reads
-      constexpr int NVA = RBR * 42;             // softmax vector instructions (approx.)
+      constexpr int NVA = RBR * (kSpread ? 30 : 42);  // softmax vector instructions (approx.)
       constexpr int VPER = (NVA + NMF - 1) / NMF;
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, NQK, 0);
+      if constexpr (!kSpread) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NQK, 0);
+      }
       if (NDS > 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int j = 0; j < NMF; ++j) {
@@ -538,9 +586,6 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     // computation next to its use in the following step).
 #pragma unroll
     for (int rb = 0; rb < RBR; ++rb) asm volatile("" ::"v"(pp[sb][rb]), "v"(l[rb]));
-    bool resc = false;
-#pragma unroll
-    for (int rb = 0; rb < RBR; ++rb) resc = resc || al[rb] != 1.f;
     if (__builtin_amdgcn_ballot_w64(resc) != 0) {
       // Everything relative to the old maximum: O (which includes the
       // products issued above), and the P of the other sub-steps still
