@@ -1030,7 +1030,7 @@ void pac_kernel(PacParams p) {
       if (t.row_count >= p.mfma_min_rows) {
         // Slabs of 16 RBR rows, TS wavefronts per slab.
         static_assert(NW == 8, "row dispatch for 8 wavefronts");
-        if (t.row_count <= 16)
+        if (t.row_count <= 32)
           mfma_piece<D, 1, 2, NW>(p, t, kvh);
         else if (t.row_count <= 128)
           mfma_piece<D, 2, 2, NW>(p, t, kvh);
