@@ -512,28 +512,23 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     // fp16 and float32): alpha is 1 and O needs no rescale in almost every
     // step.
     float al[RBR];
+    float lmx[RBR];  // one-slab layout: this lane's maximum of each row
     bool resc = false;
     if constexpr (kSpread) {
       // One slab per wavefront (compute-bound): each lane tests its own
-      // scores against the raw threshold; only when one exceeds it does the
-      // wavefront form the row maxima across the four lanes of a row (lane
-      // swaps) and move the references.
-      bool up = false;
+      // scores against the raw threshold and P is formed with the current
+      // references at once; only when a lane exceeds the threshold does the
+      // wavefront (below, after the products) form the row maxima across the
+      // four lanes of a row, move the references and form this P again.
 #pragma unroll
       for (int rb = 0; rb < RBR; ++rb) {
-        const float mx = max3(max3(x[rb][0], x[rb][1], x[rb][2]), max3(x[rb][3], x[rb][4], x[rb][5]),
-                              fmaxf(x[rb][6], x[rb][7]));
-        up = up || mx > thr[rb];
-        al[rb] = mx;  // the lane maximum, until the update below
+        lmx[rb] = max3(max3(x[rb][0], x[rb][1], x[rb][2]), max3(x[rb][3], x[rb][4], x[rb][5]),
+                       fmaxf(x[rb][6], x[rb][7]));
+        resc = resc || lmx[rb] > thr[rb];
+        al[rb] = 1.f;
       }
-      resc = __builtin_amdgcn_ballot_w64(up) != 0;
-      if (resc) {
-#pragma unroll
-        for (int rb = 0; rb < RBR; ++rb) update_ref(rb, al[rb], &al[rb]);
-      }
-      // O += P V of the same sub-step of the previous tile (P relative to the
-      // old references: rescaled with O below), issued between the vector
-      // work of the new P.
+      // O += P V of the same sub-step of the previous tile, issued between
+      // the vector work of the new P.
       if constexpr (kPrev) pv(vslot(tile - 1), ts, sb);
     } else {
       // Branch-free (the products of O += P V above overlap it): every step
@@ -546,9 +541,10 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
         resc = resc || al[rb] != 1.f;
       }
     }
-    // P = exp2(x * c - m) in the MFMA k order (slots 0..3: block 0, 4..7: block 1).
-#pragma unroll
-    for (int rb = 0; rb < RBR; ++rb) {
+    // P = exp2(x * c - m) of row block rb in the MFMA k order (slots 0..3:
+    // block 0, 4..7: block 1) into pp[sb][rb]; returns the sum of the
+    // rounded P added to `acc`.
+    auto make_p = [&](int rb, float acc) {
       float e[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(x[rb][j], c2, nm[rb]));
@@ -556,10 +552,18 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         hw[j] = pack_f16(e[2 * j], e[2 * j + 1]);
-        l[rb] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[j]), __builtin_bit_cast(f16x2, 0x3C003C00u), l[rb],
-                                       false);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[j]), __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
       }
       pp[sb][rb] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      return acc;
+    };
+    float lst[RBR];  // one-slab layout: the sum of this step's P
+#pragma unroll
+    for (int rb = 0; rb < RBR; ++rb) {
+      if constexpr (kSpread)
+        lst[rb] = make_p(rb, 0.f);
+      else
+        l[rb] = make_p(rb, l[rb]);
     }
     // Issue order: (branch-free layout: the K reads and S products, then) the
     // V^T reads and O += P V products interleaved with the vector work of the
@@ -568,12 +572,10 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
       constexpr int NQK = 2 * KS * RBR;          // products of S
       constexpr int NMF = kPrev ? DB * RBR : 1;  // products of O += P V
       constexpr int NDS = kPrev ? 2 * DB : 0;   // transpose reads
-      constexpr int NVA = RBR * (kSpread ? 30 : 42);  // softmax vector instructions (approx.)
+      constexpr int NVA = RBR * (kSpread ? 32 : 42);  // softmax vector instructions (approx.)
       constexpr int VPER = (NVA + NMF - 1) / NMF;
-      if constexpr (!kSpread) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, NQK, 0);
-      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NQK, 0);
       if (NDS > 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int j = 0; j < NMF; ++j) {
@@ -585,8 +587,16 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     // Keep the new P in this block (the compiler would otherwise sink its
     // computation next to its use in the following step).
 #pragma unroll
-    for (int rb = 0; rb < RBR; ++rb) asm volatile("" ::"v"(pp[sb][rb]), "v"(l[rb]));
+    for (int rb = 0; rb < RBR; ++rb) asm volatile("" ::"v"(pp[sb][rb]), "v"(kSpread ? lst[rb] : l[rb]));
     if (__builtin_amdgcn_ballot_w64(resc) != 0) {
+      if constexpr (kSpread) {
+        // A lane exceeded its threshold: move the references (l *= alpha),
+        // then form this step's P again relative to them.
+#pragma unroll
+        for (int rb = 0; rb < RBR; ++rb) update_ref(rb, lmx[rb], &al[rb]);
+#pragma unroll
+        for (int rb = 0; rb < RBR; ++rb) lst[rb] = make_p(rb, 0.f);
+      }
       // Everything relative to the old maximum: O (which includes the
       // products issued above), and the P of the other sub-steps still
       // waiting for their products.
@@ -600,6 +610,10 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
 #pragma unroll
           for (int rb = 0; rb < RBR; ++rb)
             pp[s2][rb] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(f16x8, pp[s2][rb]) * static_cast<_Float16>(al[rb]));
+    }
+    if constexpr (kSpread) {
+#pragma unroll
+      for (int rb = 0; rb < RBR; ++rb) l[rb] += lst[rb];
     }
   };
 
