@@ -143,6 +143,23 @@ def test_row_counts_dot_path(rows):
     check(spec, t, out, lse)
 
 
+@pytest.mark.parametrize("rows", [16, 100, 256])
+def test_reference_raised_mid_piece(rows):
+    """K grows eightfold along one 1000-token piece, so the running maximum of
+    every row rises by more than 2^8 several times after the first tile: the
+    rescale of O and of the P still waiting for its products, in the
+    branch-free (16, 100 rows) and the per-lane-test (256 rows) layouts."""
+    spec = workloads.TreeSpec(f"ramp{rows}", np.array([-1]), np.array([1000]), np.array([0]), np.array([0]),
+                              rows, 1, 128, "bf16", 81)
+    q, k, v = workloads.make_tensors(spec, "cuda")
+    ramp = torch.linspace(1.0, 8.0, 1000, device="cuda", dtype=torch.float32)
+    k = (k.float() * ramp[None, :, None]).to(torch.bfloat16).contiguous()
+    say(f"rows {rows}, K ramped x1 -> x8")
+    t, plan, out, lse = run(spec, tensors=(q, k, v), num_bins=1)
+    assert plan.view()["b_eff"][0] == 1  # one piece: every raise happens inside it
+    check(spec, t, out, lse)
+
+
 def test_max_rows_split():
     """More rows than one workgroup holds: the planner cuts row groups (> 256 rows)."""
     lens = [700] + [3] * 20
