@@ -24,6 +24,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# Dense matrix-core peaks (no sparsity): bf16 2.5 PFLOP/s; float32 inputs run
+# on the vector ALU (157.3 TFLOP/s).
+COMPUTE_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 METRIC = "logical KV tokens attended/s and unique-KV HBM GB/s (% of MI355X peak)"
 
 
@@ -223,11 +226,23 @@ def main():
             tr = json.load(f)
         if tr.get("workload") == spec.name and tr.get("kernel_source_sha") == kernel_sha():
             traffic = tr.get("hbm_bytes_per_launch")
-    result["roofline"] = {
-        "bound": "hbm", "achieved": st["unique_kv_bytes"] / (pac_avg * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-        "unit": "GB/s", "frac": st["unique_kv_bytes"] / (pac_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
-        "kernel": "pac_kernel", "algorithmic_bytes_per_launch": st["unique_kv_bytes"],
-    }
+    # Algorithmic work of one PAC launch: the unique KV bytes, and 4 d H_q
+    # FLOPs per logical (query, token) (QK^T and PV).  The bound is the larger
+    # of the two floors; the other is reported beside it.
+    flops = 4.0 * spec.head_dim * spec.num_q_heads * st["logical_tokens"]
+    cpeak = COMPUTE_PEAK_TFLOPS[spec.dtype]
+    hbm = {"bound": "hbm", "achieved": st["unique_kv_bytes"] / (pac_avg * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+           "unit": "GB/s"}
+    mfma = {"bound": "mfma" if spec.dtype == "bf16" else "alu", "achieved": flops / (pac_avg * 1e-3) / 1e12,
+            "peak": cpeak, "unit": "TFLOP/s"}
+    for r in (hbm, mfma):
+        r["frac"] = r["achieved"] / r["peak"]
+    compute_bound = flops / (cpeak * 1e12) > st["unique_kv_bytes"] / (HBM_PEAK_GBS * 1e9)
+    main, other = (mfma, hbm) if compute_bound else (hbm, mfma)
+    result["roofline"] = dict(main, traffic=traffic, kernel="pac_kernel",
+                              algorithmic_bytes_per_launch=st["unique_kv_bytes"],
+                              algorithmic_flops_per_launch=flops,
+                              secondary={k: other[k] for k in ("bound", "achieved", "peak", "unit", "frac")})
 
     if not a.no_baseline:
         print("[bench] query-guided baseline", file=sys.stderr, flush=True)
