@@ -31,8 +31,12 @@ reading taken here, implemented identically in the library, all in integers:
    lo = max_i C(rows_i, min(n_i, G)) and hi = sum_i cost(i, 1).
 6. ub_i = min(bmax_i, max(1, ceil(C(rows_i, n_i) / cost_l))).
 7. grid search k = 0..K: T_k = cost_l + (cost_l k) // K, b_i = min(ub_i, b_i(T_k));
-   the pieces (per row group) are sorted by (cost desc, node, row group,
-   piece) and each goes to the block with the smallest (load, block id).
+   7b (this build's addition): then one candidate per uniform piece length
+   U = G x 1, 2, 3, 4, 6, 8, 12, 16, ... (every node cut into pieces of U,
+   the last shorter), up to the first U that holds the longest node, as
+   k = K+1, K+2, ...; for every candidate the pieces (per row group) are
+   sorted by (cost desc, node, row group, piece) and each goes to the block
+   with the smallest (load, block id).
 8. keep the k with the smallest makespan; ties: fewer pieces, then smaller k.
 9. tasks are emitted block by block in assignment order.  The partial slot
    of (query r, node i, piece p) is slot_ptr[r] + (pieces of the nodes before
@@ -167,6 +171,23 @@ def plan(index, kv_len, g, table, m, *, r_max=256, tile=64, grid_steps=8,
                 b = min(ub[nd.i], _b_of_T(table, nd, T, G))
                 lps[nd.i] = lp_for(nd, b)
             candidates.append(lps)
+        # Step 7b: one piece length U for every node, U = G x 1, 2, 3, 4, 6,
+        # 8, 12, ... up to the first U that holds the longest node.
+        nmax = max(nd.n for nd in nodes)
+        factors = []
+        p = 1
+        while True:
+            factors.append(2 * p)  # in halves of G: U = G * f / 2
+            if G * p >= nmax:
+                break
+            if p >= 2:
+                factors.append(3 * p)
+                if G * p * 3 // 2 >= nmax:
+                    break
+            p *= 2
+        for f in factors:
+            u = G * f // 2
+            candidates.append({nd.i: u for nd in nodes})
 
     best = None
     if nodes:

@@ -133,6 +133,23 @@ void lpt(std::vector<Item>& items, int32_t m, std::vector<std::vector<Item>>* bi
 
 }  // namespace
 
+// Uniform piece lengths G x {1, 2, 3, 4, 6, 8, 12, 16, ...} in increasing
+// order, up to and including the first one that holds the longest node.
+static std::vector<int64_t> uniform_lengths(const std::vector<PNode>& nodes, int64_t G) {
+  int64_t nmax = 0;
+  for (const PNode& nd : nodes) nmax = std::max(nmax, nd.n);
+  std::vector<int64_t> us;
+  for (int64_t p = 1;; p *= 2) {
+    us.push_back(G * p);
+    if (G * p >= nmax) break;
+    if (p >= 2) {
+      us.push_back(G * p * 3 / 2);
+      if (G * p * 3 / 2 >= nmax) break;
+    }
+  }
+  return us;
+}
+
 pst_status build_plan(const TreeIndex& ix, int32_t g, const CostModel& cost, const PlanOptions& o,
                       PlanResult* out) {
   const int64_t G = o.tile;
@@ -189,6 +206,9 @@ pst_status build_plan(const TreeIndex& ix, int32_t g, const CostModel& cost, con
         lps.push_back(lp_of(nodes[a].n, std::min(ub[a], b_of_T(cost, nodes[a], T, G)), G));
       candidates.push_back(lps);
     }
+    // Candidates with one piece length for every node: U = G x {1, 2, 3, 4,
+    // 6, 8, 12, ...}, up to the first U that holds the longest node.
+    for (const int64_t u : uniform_lengths(nodes, G)) candidates.push_back(std::vector<int64_t>(nodes.size(), u));
   }
 
   std::vector<std::vector<Item>> best_bins(m);
