@@ -565,9 +565,9 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
       else
         l[rb] = make_p(rb, l[rb]);
     }
-    // Issue order: (branch-free layout: the K reads and S products, then) the
-    // V^T reads and O += P V products interleaved with the vector work of the
-    // softmax.
+    // Issue order: the K reads and S products, then the V^T reads and O +=
+    // P V products, interleaved with the vector work of the softmax
+    // (two wavefronts per slab) or followed by it (one slab per wavefront).
     {
       constexpr int NQK = 2 * KS * RBR;          // products of S
       constexpr int NMF = kPrev ? DB * RBR : 1;  // products of O += P V
@@ -577,11 +577,24 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, NQK, 0);
       if (NDS > 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      if constexpr (kSpread) {
+        // Compute-bound layout: all products, then the vector work.  Both
+        // wavefronts of a SIMD then run the same kind of work at the same
+        // time, which measured faster than interleaving the two kinds
+        // within a wavefront (the two overlap poorly across wavefronts).
 #pragma unroll
-      for (int j = 0; j < NMF; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);
-        if (j + 4 < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int j = 0; j < NMF; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (j + 4 < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x002, NVA + 40, 0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NMF; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);
+          if (j + 4 < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
     }
     // Keep the new P in this block (the compiler would otherwise sink its
