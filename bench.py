@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the warm-cache timing (every PAC launch of the run is then cold, as under a profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="> 0: K/V in a paged pool of pages of this many tokens (scattered, with holes)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "pac_traffic.json"),
                     help="rocprofv3 counter summary giving the PAC kernel's HBM bytes")
     return ap.parse_args()
@@ -157,8 +159,13 @@ def main():
     spec = workloads.config(a.config)
     print(f"[bench] workload {spec.name}: generating inputs", file=sys.stderr, flush=True)
     q, k, v = workloads.make_tensors(spec, "cuda")
+    # The kernels read kk, vv (the contiguous pools, or a paged copy); the
+    # oracle sample reads the contiguous k, v.
+    kk, vv, paged = k, v, None
+    if a.page_size > 0:
+        paged, kk, vv = workloads.page_pools(spec, k, v, a.page_size, fill=0.0)
     t0 = time.perf_counter()
-    tree = pst.Tree.from_spec(spec, out_dtype="f32")
+    tree = pst.Tree.from_paged(spec, paged, out_dtype="f32") if paged else pst.Tree.from_spec(spec, out_dtype="f32")
     t_tree = (time.perf_counter() - t0) * 1e3
     t0 = time.perf_counter()
     plan = pst.Plan(tree)
@@ -171,11 +178,11 @@ def main():
     evict_bufs = (torch.empty(1 << 30, dtype=torch.uint8, device="cuda"), torch.empty(4096, dtype=torch.float32, device="cuda"))
 
     print(f"[bench] timing {a.steps} cold steps", file=sys.stderr, flush=True)
-    pac_ms, por_ms, wall = time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, a.steps, a.warmup)
+    pac_ms, por_ms, wall = time_steps(torch, pst, plan, q, kk, vv, out, lse, ws, evict_bufs, a.steps, a.warmup)
     step_ms = [x + y for x, y in zip(pac_ms, por_ms)]
     ms = statistics.mean(step_ms)
     pac_avg = statistics.mean(pac_ms)
-    warm_ms = None if a.no_warm else time_warm(torch, pst, plan, q, k, v, out, lse, ws, a.steps)
+    warm_ms = None if a.no_warm else time_warm(torch, pst, plan, q, kk, vv, out, lse, ws, a.steps)
 
     # Achievable streaming read bandwidth (same 128-bit loads, 2 GiB).
     rd = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
@@ -206,7 +213,8 @@ def main():
         "config": {"workload": spec.name, "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
                    "head_dim": spec.head_dim, "nodes": spec.num_nodes, "queries": spec.num_queries,
                    "unique_kv_tokens": st["unique_kv_tokens"], "logical_tokens": st["logical_tokens"],
-                   "cache": "cold (1 GiB read of an unrelated buffer before each step)", "plan_reused": True},
+                   "cache": "cold (1 GiB read of an unrelated buffer before each step)", "plan_reused": True,
+                   "kv_layout": f"paged, {a.page_size}-token pages" if paged else "contiguous"},
         "unique_kv_GBps": st["unique_kv_bytes"] / (ms * 1e-3) / 1e9,
         "unique_kv_frac_of_peak": st["unique_kv_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "pac_ms": pac_avg,
@@ -224,7 +232,7 @@ def main():
     if os.path.exists(a.traffic):
         with open(a.traffic) as f:
             tr = json.load(f)
-        if tr.get("workload") == spec.name and tr.get("kernel_source_sha") == kernel_sha():
+        if tr.get("workload") == spec.name and tr.get("kernel_source_sha") == kernel_sha() and not paged:
             traffic = tr.get("hbm_bytes_per_launch")
     # Algorithmic work of one PAC launch: the unique KV bytes, and 4 d H_q
     # FLOPs per logical (query, token) (QK^T and PV).  The bound is the larger
@@ -248,7 +256,7 @@ def main():
         print("[bench] query-guided baseline", file=sys.stderr, flush=True)
         bplan = pst.Plan(tree, query_guided=True)
         bws = pst.workspace(bplan)
-        bpac, bpor, _ = time_steps(torch, pst, bplan, q, k, v, out, lse, bws, evict_bufs, max(3, a.steps // 4), 1)
+        bpac, bpor, _ = time_steps(torch, pst, bplan, q, kk, vv, out, lse, bws, evict_bufs, max(3, a.steps // 4), 1)
         bms = statistics.mean([x + y for x, y in zip(bpac, bpor)])
         result["baseline_query_guided"] = {
             "ms_per_step": bms, "speedup_of_tree_path": bms / ms,
@@ -258,7 +266,7 @@ def main():
         del bws
         # The tree path's output is recomputed below for the parity sample.
     evict(pst, evict_bufs)
-    pst.decode_attn(plan, q, k, v, out=out, lse=lse, ws=ws)
+    pst.decode_attn(plan, q, kk, vv, out=out, lse=lse, ws=ws)
     torch.cuda.synchronize()
     if not a.no_cpu_baseline:
         print("[bench] oracle on a bounded sample (cpu_baseline)", file=sys.stderr, flush=True)

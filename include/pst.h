@@ -79,7 +79,8 @@ typedef struct pst_cost_s* pst_cost_model_t;
  * copied; the caller keeps ownership.
  *   parent[i]      in [-1, i): the node whose tokens precede node i's; -1 =
  *                  child of the virtual root.  Parents come before children.
- *   kv_offset[i]   >= 0: first token of node i in the K/V pools.
+ *   kv_offset[i]   >= 0: first token of node i in the K/V pools (contiguous
+ *                  layout; may be NULL when page_size > 0).
  *   kv_len[i]      >= 1: tokens in node i.
  *   query_node[r]  in [0, num_nodes): the deepest node on query r's path.
  *   node_masked    NULL or [num_nodes]: 1 = node i is masked (kv_len <= 64).
@@ -87,6 +88,21 @@ typedef struct pst_cost_s* pst_cost_model_t;
  *                  masked, bit j set = token j of that node visible.  Ignored
  *                  for queries on unmasked nodes.  Ancestors of a query's
  *                  node are always visible in full.
+ *   page_size      0: each node is one contiguous run of the pools from
+ *                  kv_offset[i].  > 0 (a power of two in [8, 65536]): paged
+ *                  K/V, the layout of a paged KV cache (the FlashDecoding-
+ *                  compatible input CoDec's implementation section takes):
+ *                  token j of node i sits in pool row
+ *                      page_idx[page_ptr[i] + j / page_size] * page_size
+ *                        + j % page_size.
+ *   page_ptr       [num_nodes + 1] when page_size > 0: page_ptr[0] = 0,
+ *                  non-decreasing; node i owns the pages
+ *                  page_idx[page_ptr[i] .. page_ptr[i+1]), at least
+ *                  ceil(kv_len[i] / page_size) of them (growth through
+ *                  pst_tree_set_lengths stays within them).
+ *   page_idx       [page_ptr[num_nodes]] page numbers >= 0; every page lies
+ *                  inside the pools (pool_tokens, or 0 = (largest page + 1)
+ *                  * page_size).  Pages may be shared or in any order.
  * Every query must see at least one token. */
 typedef struct {
   int32_t num_nodes;
@@ -97,6 +113,9 @@ typedef struct {
   const int32_t* query_node;
   const uint64_t* query_mask;
   const uint8_t* node_masked;
+  int32_t page_size;
+  const int32_t* page_ptr;
+  const int32_t* page_idx;
 } pst_tree_desc;
 
 /* Head layout and dtypes.  head_dim in {64, 128}; num_q_heads a multiple of
@@ -149,6 +168,9 @@ typedef struct {
   const int32_t* nq_idx;    /* [num_entries] */
   const uint64_t* nq_mask;  /* [num_entries] */
   const int64_t* visible;   /* [num_queries] tokens each query sees */
+  int32_t page_size;        /* 0 = contiguous K/V */
+  const int32_t* page_ptr;  /* [num_nodes + 1] when paged, else NULL */
+  const int32_t* page_idx;  /* [page_ptr[num_nodes]] when paged, else NULL */
 } pst_index_view;
 pst_status pst_tree_get_index(pst_tree_t tree, pst_index_view* view);
 

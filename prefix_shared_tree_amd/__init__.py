@@ -70,7 +70,8 @@ class PstError(RuntimeError):
 class _TreeDesc(C.Structure):
     _fields_ = [("num_nodes", C.c_int32), ("parent", C.c_void_p), ("kv_offset", C.c_void_p),
                 ("kv_len", C.c_void_p), ("num_queries", C.c_int32), ("query_node", C.c_void_p),
-                ("query_mask", C.c_void_p), ("node_masked", C.c_void_p)]
+                ("query_mask", C.c_void_p), ("node_masked", C.c_void_p), ("page_size", C.c_int32),
+                ("page_ptr", C.c_void_p), ("page_idx", C.c_void_p)]
 
 
 class _Shape(C.Structure):
@@ -82,7 +83,8 @@ class _Shape(C.Structure):
 class _IndexView(C.Structure):
     _fields_ = [("num_nodes", C.c_int32), ("num_queries", C.c_int32), ("num_entries", C.c_int64),
                 ("depth", C.c_void_p), ("n_q", C.c_void_p), ("qn_ptr", C.c_void_p), ("qn_idx", C.c_void_p),
-                ("nq_ptr", C.c_void_p), ("nq_idx", C.c_void_p), ("nq_mask", C.c_void_p), ("visible", C.c_void_p)]
+                ("nq_ptr", C.c_void_p), ("nq_idx", C.c_void_p), ("nq_mask", C.c_void_p), ("visible", C.c_void_p),
+                ("page_size", C.c_int32), ("page_ptr", C.c_void_p), ("page_idx", C.c_void_p)]
 
 
 class _PlanOpts(C.Structure):
@@ -168,17 +170,31 @@ def _dtype_code(dtype) -> int:
 
 
 class Tree:
-    """A validated tree and its index (``pst_tree_build``)."""
+    """A validated tree and its index (``pst_tree_build``).
+
+    Contiguous K/V: node i is the run of ``kv_len[i]`` pool rows from
+    ``kv_offset[i]``.  Paged K/V (``page_size`` > 0, ``kv_offset`` may be
+    None): token j of node i is pool row
+    ``page_idx[page_ptr[i] + j // page_size] * page_size + j % page_size``.
+    """
 
     def __init__(self, parent, kv_offset, kv_len, query_node, *, num_q_heads, num_kv_heads, head_dim,
                  dtype="bf16", out_dtype=None, query_mask=None, node_masked=None, scale=0.0,
-                 kv_stride_head=0, kv_stride_token=0, pool_tokens=0, host_only=False, stream=None):
+                 kv_stride_head=0, kv_stride_token=0, pool_tokens=0, page_size=0, page_ptr=None, page_idx=None,
+                 host_only=False, stream=None):
         self._h = C.c_void_p()
         parent, p_parent = _arr(parent, np.int32)
-        kv_offset, p_off = _arr(kv_offset, np.int64)
         kv_len, p_len = _arr(kv_len, np.int32)
+        if kv_offset is None:
+            kv_offset = np.zeros(len(kv_len), dtype=np.int64)
+        kv_offset, p_off = _arr(kv_offset, np.int64)
         query_node, p_qn = _arr(query_node, np.int32)
         keep = [parent, kv_offset, kv_len, query_node]
+        p_pp = p_pi = None
+        if page_size:
+            page_ptr, p_pp = _arr(page_ptr, np.int32)
+            page_idx, p_pi = _arr(page_idx if page_idx is not None else np.zeros(0), np.int32)
+            keep += [page_ptr, page_idx]
         p_qm = p_nm = None
         if query_mask is not None:
             qm, p_qm = _arr(query_mask, np.uint64)
@@ -186,7 +202,8 @@ class Tree:
         if node_masked is not None:
             nm, p_nm = _arr(node_masked, np.uint8)
             keep.append(nm)
-        desc = _TreeDesc(len(parent), p_parent, p_off, p_len, len(query_node), p_qn, p_qm, p_nm)
+        desc = _TreeDesc(len(parent), p_parent, p_off, p_len, len(query_node), p_qn, p_qm, p_nm, int(page_size),
+                         p_pp, p_pi)
         self.in_dtype = _dtype_code(dtype)
         self.out_dtype = self.in_dtype if out_dtype is None else _dtype_code(out_dtype)
         shape = _Shape(num_q_heads, num_kv_heads, head_dim, self.in_dtype, self.out_dtype, scale,
@@ -199,8 +216,14 @@ class Tree:
         self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
         self.num_nodes, self.num_queries = len(parent), len(query_node)
         self.host_only = host_only
+        self.page_size = int(page_size)
         # Elements the K/V layout addresses (the last channel of the last token of the last head).
-        pool = pool_tokens if pool_tokens > 0 else (int((kv_offset + kv_len).max()) if len(kv_len) else 0)
+        if pool_tokens > 0:
+            pool = pool_tokens
+        elif page_size:
+            pool = (int(page_idx.max()) + 1) * int(page_size) if len(page_idx) else 0
+        else:
+            pool = int((kv_offset + kv_len).max()) if len(kv_len) else 0
         st_tok = kv_stride_token if kv_stride_token > 0 else head_dim
         st_head = kv_stride_head if kv_stride_head > 0 else pool * head_dim
         self.kv_extent = 0 if pool == 0 else (num_kv_heads - 1) * st_head + (pool - 1) * st_tok + head_dim
@@ -212,6 +235,15 @@ class Tree:
                    num_kv_heads=spec.num_kv_heads, head_dim=spec.head_dim, dtype=spec.dtype,
                    query_mask=spec.query_mask, node_masked=spec.node_masked, **kw)
 
+    @classmethod
+    def from_paged(cls, spec, paged, **kw):
+        """Build ``spec``'s tree over a paged pool: ``paged`` holds ``page_size``,
+        ``page_ptr`` and ``page_idx`` (see ``workloads.page_pools``)."""
+        return cls(spec.parent, None, spec.kv_len, spec.query_node, num_q_heads=spec.num_q_heads,
+                   num_kv_heads=spec.num_kv_heads, head_dim=spec.head_dim, dtype=spec.dtype,
+                   query_mask=spec.query_mask, node_masked=spec.node_masked, page_size=paged["page_size"],
+                   page_ptr=paged["page_ptr"], page_idx=paged["page_idx"], **kw)
+
     def index(self) -> dict:
         v = _IndexView()
         _check(_lib.pst_tree_get_index(self._h, C.byref(v)))
@@ -221,6 +253,10 @@ class Tree:
             "qn_ptr": _view(v.qn_ptr, B + 1, np.int32), "qn_idx": _view(v.qn_idx, E, np.int32),
             "nq_ptr": _view(v.nq_ptr, N + 1, np.int32), "nq_idx": _view(v.nq_idx, E, np.int32),
             "nq_mask": _view(v.nq_mask, E, np.uint64), "visible": _view(v.visible, B, np.int64),
+            "page_size": int(v.page_size),
+            "page_ptr": _view(v.page_ptr, N + 1, np.int32) if v.page_size else None,
+            "page_idx": (_view(v.page_idx, int(_view(v.page_ptr, N + 1, np.int32)[-1]), np.int32)
+                         if v.page_size else None),
         }
 
     def set_lengths(self, kv_len, stream=None):

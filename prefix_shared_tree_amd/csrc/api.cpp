@@ -79,6 +79,8 @@ struct pst_tree_s {
   std::vector<pst_plan_s*> plans;  // live plans: their device tasks follow length changes
   int64_t* d_node_off = nullptr;
   int32_t* d_node_len = nullptr;
+  int32_t* d_page_ptr = nullptr;
+  int32_t* d_page_idx = nullptr;
   uint8_t* d_node_masked = nullptr;
   int32_t* d_nq_ptr = nullptr;
   int32_t* d_nq_idx = nullptr;
@@ -107,6 +109,8 @@ struct pst_cost_s {
 static void free_tree_device(pst_tree_s* t) {
   dev_free(t->d_node_off);
   dev_free(t->d_node_len);
+  dev_free(t->d_page_ptr);
+  dev_free(t->d_page_idx);
   dev_free(t->d_node_masked);
   dev_free(t->d_nq_ptr);
   dev_free(t->d_nq_idx);
@@ -182,11 +186,16 @@ pst_status pst_tree_build(const pst_tree_desc* desc, const pst_shape* shape, uin
   t->shape = *shape;
   if (t->shape.scale <= 0.f) t->shape.scale = 1.0f / std::sqrt(static_cast<float>(shape->head_dim));
   int64_t need = 0;
-  for (int32_t i = 0; i < t->ix.N; ++i) need = std::max(need, t->ix.kv_offset[i] + t->ix.kv_len[i]);
+  if (t->ix.page_size > 0) {
+    for (const int32_t pg : t->ix.page_idx) need = std::max(need, (static_cast<int64_t>(pg) + 1) * t->ix.page_size);
+  } else {
+    for (int32_t i = 0; i < t->ix.N; ++i) need = std::max(need, t->ix.kv_offset[i] + t->ix.kv_len[i]);
+  }
   t->pool_tokens = shape->pool_tokens > 0 ? shape->pool_tokens : need;
   if (need > t->pool_tokens) {
     delete t;
-    set_error("a node lies outside the K/V pools (pool_tokens too small)");
+    set_error(t->ix.page_size > 0 ? "a page lies outside the K/V pools (pool_tokens too small)"
+                                  : "a node lies outside the K/V pools (pool_tokens too small)");
     return PST_E_INVALID_TREE;
   }
   if (t->shape.kv_stride_token == 0) t->shape.kv_stride_token = shape->head_dim;
@@ -213,6 +222,9 @@ pst_status pst_tree_build(const pst_tree_desc* desc, const pst_shape* shape, uin
     const TreeIndex& ix = t->ix;
     st = dev_upload(&t->d_node_off, ix.kv_offset.data(), ix.N, s);
     if (st == PST_OK) st = dev_upload(&t->d_node_len, ix.kv_len.data(), ix.N, s);
+    if (st == PST_OK && ix.page_size > 0) st = dev_upload(&t->d_page_ptr, ix.page_ptr.data(), ix.page_ptr.size(), s);
+    if (st == PST_OK && ix.page_size > 0 && !ix.page_idx.empty())
+      st = dev_upload(&t->d_page_idx, ix.page_idx.data(), ix.page_idx.size(), s);
     if (st == PST_OK) st = dev_upload(&t->d_node_masked, ix.masked.data(), ix.N, s);
     if (st == PST_OK) st = dev_upload(&t->d_nq_ptr, ix.nq_ptr.data(), ix.nq_ptr.size(), s);
     if (st == PST_OK) st = dev_upload(&t->d_nq_idx, ix.nq_idx.data(), ix.nq_idx.size(), s);
@@ -249,7 +261,12 @@ pst_status pst_tree_set_lengths(pst_tree_t t, const int32_t* kv_len, void* strea
       set_error("masked node " + std::to_string(i) + " would exceed 64 tokens");
       return PST_E_INVALID_TREE;
     }
-    if (ix.kv_offset[i] + kv_len[i] > t->pool_tokens) {
+    if (ix.page_size > 0) {
+      if (static_cast<int64_t>(ix.page_ptr[i + 1] - ix.page_ptr[i]) * ix.page_size < kv_len[i]) {
+        set_error("node " + std::to_string(i) + " would outgrow its pages");
+        return PST_E_INVALID_TREE;
+      }
+    } else if (ix.kv_offset[i] + kv_len[i] > t->pool_tokens) {
       set_error("node " + std::to_string(i) + " would leave the K/V pools");
       return PST_E_INVALID_TREE;
     }
@@ -312,6 +329,9 @@ pst_status pst_tree_get_index(pst_tree_t t, pst_index_view* v) {
   v->nq_idx = ix.nq_idx.data();
   v->nq_mask = ix.nq_mask.data();
   v->visible = ix.visible.data();
+  v->page_size = ix.page_size;
+  v->page_ptr = ix.page_size > 0 ? ix.page_ptr.data() : nullptr;
+  v->page_idx = ix.page_size > 0 ? ix.page_idx.data() : nullptr;
   return PST_OK;
 }
 
@@ -467,7 +487,8 @@ pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* op
     for (size_t i = 0; i < dt.size(); ++i) {
       const Task& a = p->r.tasks[i];
       DevTask& b = dt[i];
-      b.tok0 = t->ix.kv_offset[a.node] + a.kv_begin;
+      // Contiguous: the piece's first pool token; paged: its position in the node.
+      b.tok0 = t->ix.page_size > 0 ? a.kv_begin : t->ix.kv_offset[a.node] + a.kv_begin;
       b.node = a.node;
       b.kv_begin = a.kv_begin;
       b.kv_len = a.kv_len;
@@ -592,6 +613,9 @@ pst_status pst_pac(pst_plan_t p, const void* q, const void* k, const void* v, vo
   pp.tasks = p->d_tasks;
   pp.bin_ptr = p->d_bin_ptr;
   pp.nq_idx = t->d_nq_idx;
+  pp.page_ptr = t->d_page_ptr;
+  pp.page_idx = t->d_page_idx;
+  pp.page_shift = t->ix.page_size > 0 ? __builtin_ctz(static_cast<unsigned>(t->ix.page_size)) : -1;
   pp.nq_mask = t->d_nq_mask;
   pp.entry_slot = p->d_entry_slot;
   pp.stride_head = t->shape.kv_stride_head;

@@ -30,15 +30,37 @@ pst_status build_tree_index(const pst_tree_desc& d, TreeIndex* out) {
     set_error("negative node or query count");
     return PST_E_INVALID_ARG;
   }
-  if ((N > 0 && (!d.parent || !d.kv_offset || !d.kv_len)) || (B > 0 && !d.query_node)) {
+  const bool paged = d.page_size != 0;
+  if ((N > 0 && (!d.parent || (!paged && !d.kv_offset) || !d.kv_len)) || (B > 0 && !d.query_node) ||
+      (paged && (!d.page_ptr || (N > 0 && d.page_ptr[N] > 0 && !d.page_idx)))) {
     set_error("null tree array");
+    return PST_E_INVALID_ARG;
+  }
+  if (paged && (d.page_size < 8 || d.page_size > 65536 || (d.page_size & (d.page_size - 1)) != 0)) {
+    set_error("page_size must be 0 or a power of two in [8, 65536]");
     return PST_E_INVALID_ARG;
   }
   t.N = N;
   t.B = B;
   t.parent.assign(d.parent, d.parent + N);
   t.kv_len.assign(d.kv_len, d.kv_len + N);
-  t.kv_offset.assign(d.kv_offset, d.kv_offset + N);
+  if (paged) {
+    // Paged K/V: validate the page table; kv_offset is unused (zeros).
+    t.page_size = d.page_size;
+    t.kv_offset.assign(N, 0);
+    t.page_ptr.assign(d.page_ptr, d.page_ptr + N + 1);
+    if (t.page_ptr[0] != 0) return bad("page_ptr[0] != 0");
+    for (int32_t i = 0; i < N; ++i) {
+      if (t.page_ptr[i + 1] < t.page_ptr[i]) return bad("page_ptr decreases at node " + std::to_string(i));
+      if (static_cast<int64_t>(t.page_ptr[i + 1] - t.page_ptr[i]) * d.page_size < d.kv_len[i])
+        return bad("node " + std::to_string(i) + " has fewer pages than its tokens need");
+    }
+    t.page_idx.assign(d.page_idx, d.page_idx + t.page_ptr[N]);
+    for (size_t k = 0; k < t.page_idx.size(); ++k)
+      if (t.page_idx[k] < 0) return bad("page_idx[" + std::to_string(k) + "] < 0");
+  } else {
+    t.kv_offset.assign(d.kv_offset, d.kv_offset + N);
+  }
   t.query_node.assign(d.query_node, d.query_node + B);
   t.masked.assign(N, 0);
   if (d.node_masked)

@@ -190,10 +190,32 @@ struct Geo {
 };
 
 struct TaskInfo {
-  int piece, kv_begin, kv_len, row_begin, row_count, e0, masked;
-  const char* kbase;  // K of this kv head at the piece's first token
+  int piece, kv_begin, kv_len, row_begin, row_count, e0, masked, node;
+  const char* kbase;  // K of this kv head at the piece's first token (paged: at the pool's first row)
   const char* vbase;
 };
+
+// Paged K/V: the pool row of the first token of 1 KB DMA block b of `tile`,
+// and the valid tokens of that block (tpb tokens per block; a block never
+// crosses a page: pages hold a power of two >= 8 tokens and pieces start at
+// multiples of 64).  Page-table reads are scalar (wave-uniform indices).
+struct PagedBlock {
+  int64_t row;
+  int valid;
+};
+__device__ __forceinline__ PagedBlock paged_block(const PacParams& p, const TaskInfo& t, int tile_tok, int b,
+                                                  int tpb) {
+  const auto* ptr = (const __attribute__((address_space(4))) int32_t*)(p.page_ptr);
+  const auto* idx = (const __attribute__((address_space(4))) int32_t*)(p.page_idx);
+  const int tb = tile_tok + b * tpb;  // first token of the block, from the piece start
+  PagedBlock r;
+  r.valid = max(0, min(tpb, t.kv_len - tb));
+  const int pos = t.kv_begin + tb;  // position in the node
+  // A block past the piece's end reads nothing; it still names a valid page.
+  const int slot = ptr[t.node] + (r.valid > 0 ? (pos >> p.page_shift) : 0);
+  r.row = (static_cast<int64_t>(idx[slot]) << p.page_shift) + (pos & ((1 << p.page_shift) - 1));
+  return r;
+}
 
 // Row r of the task -> (query entry, q-head); returns false past the task's rows.
 __device__ __forceinline__ bool row_target(const PacParams& p, const TaskInfo& t, int kvh, int r, int* entry,
@@ -222,14 +244,31 @@ __device__ __forceinline__ void write_partial(const PacParams& p, const TaskInfo
 template <int NW>
 constexpr int kHalfOps = TILE_BYTES / 1024 / NW;  // DMA operations per thread for one K (or V) tile
 template <int D, int EB, int NW>
-__device__ __forceinline__ void issue_tile(const TaskInfo& t, int64_t stb, int tile, int stage, int tid) {
+__device__ __forceinline__ void issue_tile(const PacParams& p, const TaskInfo& t, int64_t stb, int tile, int stage,
+                                           int tid) {
   using G = Geo<D, EB>;
+  constexpr int TPB = 64 / G::CPT;  // tokens per 1 KB block
   const int tok_base = tile * G::TT;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  char* st = pac_lds + stage * STAGE_BYTES;
+  if (p.page_shift >= 0) {
+#pragma unroll
+    for (int c = 0; c < kHalfOps<NW>; ++c) {
+      const int b = c * NW + w;
+      const PagedBlock pb = paged_block(p, t, tok_base, b, TPB);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(t.kbase + pb.row * stb, pb.valid * stb);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(t.vbase + pb.row * stb, pb.valid * stb);
+      const int P = b * 64 + lane;
+      const int tok = P / G::CPT, phys = P % G::CPT;
+      const int voff = static_cast<int>((tok - b * TPB) * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4);
+      dma16(rk, voff, lds_addr(st + b * 1024));
+      dma16(rv, voff, lds_addr(st + TILE_BYTES + b * 1024));
+    }
+    return;
+  }
   const int64_t bytes = static_cast<int64_t>(min(G::TT, t.kv_len - tok_base)) * stb;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(t.kbase + tok_base * stb, bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(t.vbase + tok_base * stb, bytes);
-  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  char* st = pac_lds + stage * STAGE_BYTES;
 #pragma unroll
   for (int c = 0; c < kHalfOps<NW>; ++c) {
     const int b = c * NW + w;
@@ -243,26 +282,26 @@ __device__ __forceinline__ void issue_tile(const TaskInfo& t, int64_t stb, int t
 
 // Tiles 0 .. NSTAGE-2 (issued before the queries are gathered).
 template <int D, int EB, int NW>
-__device__ __forceinline__ void issue_prologue(const TaskInfo& t, int64_t stb, int tid) {
+__device__ __forceinline__ void issue_prologue(const PacParams& p, const TaskInfo& t, int64_t stb, int tid) {
   using G = Geo<D, EB>;
   const int ntiles = (t.kv_len + G::TT - 1) / G::TT;
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i)
-    if (i < ntiles) issue_tile<D, EB, NW>(t, stb, i, i, tid);
+    if (i < ntiles) issue_tile<D, EB, NW>(p, t, stb, i, i, tid);
 }
 
 // The tile loop: wait for tile i (2 kHalfOps DMA operations per thread and tile), a
 // barrier without a memory fence (which would drain every DMA in flight),
 // refill the stage of tile i-1 with tile i+3, compute tile i.
 template <int D, int EB, int NW, typename F>
-__device__ __forceinline__ void run_tiles(const TaskInfo& t, int64_t stb, int tid, F&& compute) {
+__device__ __forceinline__ void run_tiles(const PacParams& p, const TaskInfo& t, int64_t stb, int tid, F&& compute) {
   using G = Geo<D, EB>;
   const int ntiles = (t.kv_len + G::TT - 1) / G::TT;
   for (int tile = 0; tile < ntiles; ++tile) {
     wait_vmem_n(2 * kHalfOps<NW> * min(NSTAGE - 2, ntiles - 1 - tile));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");  // no LDS access moves above the barrier
-    if (tile + NSTAGE - 1 < ntiles) issue_tile<D, EB, NW>(t, stb, tile + NSTAGE - 1, (tile + NSTAGE - 1) % NSTAGE, tid);
+    if (tile + NSTAGE - 1 < ntiles) issue_tile<D, EB, NW>(p, t, stb, tile + NSTAGE - 1, (tile + NSTAGE - 1) % NSTAGE, tid);
     compute(pac_lds + (tile % NSTAGE) * STAGE_BYTES, tile);
   }
 }
@@ -294,12 +333,27 @@ __device__ __forceinline__ char* vslot(int j) { return pac_lds + (j % NSTAGE) * 
 // writes kHalfOps 1 KB blocks; lane L of block b fills chunk position
 // P = 64 b + L, i.e. token P / CPT, chunk (P % CPT) ^ (token % CPT).
 template <int D, int NW>
-__device__ __forceinline__ void issue_half(const char* base, int kv_len, int64_t stb, int tile, char* dst, int tid) {
+__device__ __forceinline__ void issue_half(const PacParams& p, const TaskInfo& t, const char* base, int64_t stb,
+                                           int tile, char* dst, int tid) {
   using G = Geo<D, 2>;
+  constexpr int TPB = 64 / G::CPT;  // tokens per 1 KB block
   const int tok_base = tile * G::TT;
-  const int64_t bytes = static_cast<int64_t>(min(G::TT, kv_len - tok_base)) * stb;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(base + tok_base * stb, bytes);
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (p.page_shift >= 0) {
+#pragma unroll
+    for (int c = 0; c < kHalfOps<NW>; ++c) {
+      const int b = c * NW + w;
+      const PagedBlock pb = paged_block(p, t, tok_base, b, TPB);
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(base + pb.row * stb, pb.valid * stb);
+      const int P = b * 64 + lane;
+      const int tok = P / G::CPT, phys = P % G::CPT;
+      dma16(r, static_cast<int>((tok - b * TPB) * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4),
+            lds_addr(dst + b * 1024));
+    }
+    return;
+  }
+  const int64_t bytes = static_cast<int64_t>(min(G::TT, t.kv_len - tok_base)) * stb;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base + tok_base * stb, bytes);
 #pragma unroll
   for (int c = 0; c < kHalfOps<NW>; ++c) {
     const int b = c * NW + w;
@@ -384,11 +438,11 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     for (int o = 0; o < QOPS; ++o)
       if (o * NW + w < qops_total) dma16(rq, static_cast<int>(qoff[o]), lds_addr(qarea + (o * NW + w) * 1024));
   }
-  if (0 < nt) issue_half<D, NW>(t.kbase, t.kv_len, stb, 0, kslot(0), tid);
-  if (1 < nt) issue_half<D, NW>(t.kbase, t.kv_len, stb, 1, kslot(1), tid);
-  if (0 < nt) issue_half<D, NW>(t.vbase, t.kv_len, stb, 0, vslot(0), tid);
-  if (2 < nt) issue_half<D, NW>(t.kbase, t.kv_len, stb, 2, kslot(2), tid);
-  if (1 < nt) issue_half<D, NW>(t.vbase, t.kv_len, stb, 1, vslot(1), tid);
+  if (0 < nt) issue_half<D, NW>(p, t, t.kbase, stb, 0, kslot(0), tid);
+  if (1 < nt) issue_half<D, NW>(p, t, t.kbase, stb, 1, kslot(1), tid);
+  if (0 < nt) issue_half<D, NW>(p, t, t.vbase, stb, 0, vslot(0), tid);
+  if (2 < nt) issue_half<D, NW>(p, t, t.kbase, stb, 2, kslot(2), tid);
+  if (1 < nt) issue_half<D, NW>(p, t, t.vbase, stb, 1, vslot(1), tid);
 
   bf16x8 qf[RBR][KS];
   f32x4 o[DB][RBR];
@@ -486,8 +540,8 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
       // and eight wavefronts issuing together right after a barrier queue up
       // behind each other.  (Bandwidth-bound layouts refill at the barrier,
       // as early as possible.)
-      if (kSpread && sb == 0 && tile + 3 < nt) issue_half<D, NW>(t.kbase, t.kv_len, stb, tile + 3, kslot(tile + 3), tid);
-      if (kSpread && sb == NSUB - 1 && tile + 2 < nt) issue_half<D, NW>(t.vbase, t.kv_len, stb, tile + 2, vslot(tile + 2), tid);
+      if (kSpread && sb == 0 && tile + 3 < nt) issue_half<D, NW>(p, t, t.kbase, stb, tile + 3, kslot(tile + 3), tid);
+      if (kSpread && sb == NSUB - 1 && tile + 2 < nt) issue_half<D, NW>(p, t, t.vbase, stb, tile + 2, vslot(tile + 2), tid);
       if constexpr (!kSpread) pv(vslot(tile - 1), ts, sb);
     }
     // Raw scores; lane holds tokens 4 lg + i of each 16-token block, row l16.
@@ -644,8 +698,8 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     // in the steps of tile i when `refill` is false; at i = 0 the refill
     // targets hold the queries: after the reads below).
     if (i > 0 && refill) {
-      if (i + 3 < nt) issue_half<D, NW>(t.kbase, t.kv_len, stb, i + 3, kslot(i + 3), tid);
-      if (i + 2 < nt) issue_half<D, NW>(t.vbase, t.kv_len, stb, i + 2, vslot(i + 2), tid);
+      if (i + 3 < nt) issue_half<D, NW>(p, t, t.kbase, stb, i + 3, kslot(i + 3), tid);
+      if (i + 2 < nt) issue_half<D, NW>(p, t, t.vbase, stb, i + 2, vslot(i + 2), tid);
     }
     if (i == 0) {
       if (active) {
@@ -676,8 +730,8 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (i == 0) {
-      if (3 < nt) issue_half<D, NW>(t.kbase, t.kv_len, stb, 3, kslot(3), tid);
-      if (2 < nt) issue_half<D, NW>(t.vbase, t.kv_len, stb, 2, vslot(2), tid);
+      if (3 < nt) issue_half<D, NW>(p, t, t.kbase, stb, 3, kslot(3), tid);
+      if (2 < nt) issue_half<D, NW>(p, t, t.vbase, stb, 2, vslot(2), tid);
     }
   };
   // The NSUB steps of tile i (tile 0: no products of a previous tile).
@@ -837,7 +891,7 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
   const int R = t.row_count;
   const int r0 = rs * RL;
 
-  issue_prologue<D, EB, NW>(t, stb, tid);
+  issue_prologue<D, EB, NW>(p, t, stb, tid);
 
   // Branch-free gather (dead rows read row 0 of the task and are zeroed).
   uint32_t q[RL][4];
@@ -947,7 +1001,7 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
     }
   };
 
-  run_tiles<D, EB, NW>(t, stb, tid, compute);
+  run_tiles<D, EB, NW>(p, t, stb, tid, compute);
 
   // Merge the TPI token streams of this row split (lanes li, li + LPT, ...).
   for (int off = LPT; off < LPS; off <<= 1) {
@@ -1049,7 +1103,10 @@ void pac_kernel(PacParams p) {
     t.masked = (__builtin_amdgcn_readfirstlane(task.flags) & kDevMasked) != 0;
     const int64_t tok0 = (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(task.tok0 >> 32))) << 32) |
                          static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(task.tok0)));
-    const int64_t off = (kvh * p.stride_head + tok0 * p.stride_token) * esz;
+    t.node = __builtin_amdgcn_readfirstlane(task.node);
+    // Contiguous: K/V at the piece's first token; paged: the head's pool
+    // start (blocks add their page rows).
+    const int64_t off = (kvh * p.stride_head + (p.page_shift >= 0 ? 0 : tok0) * p.stride_token) * esz;
     t.kbase = static_cast<const char*>(p.k) + off;
     t.vbase = static_cast<const char*>(p.v) + off;
     bool done = false;

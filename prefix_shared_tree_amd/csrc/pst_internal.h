@@ -65,7 +65,9 @@ struct TreeIndex {
   int32_t N = 0, B = 0;
   bool have_mask = false;
   std::vector<int32_t> parent, kv_len, query_node;
-  std::vector<int64_t> kv_offset;
+  std::vector<int64_t> kv_offset;  // contiguous layout (zeros when paged)
+  int32_t page_size = 0;           // > 0: paged layout
+  std::vector<int32_t> page_ptr, page_idx;
   std::vector<uint8_t> masked;
   std::vector<uint64_t> qmask;
   std::vector<int32_t> depth, n_q, qn_ptr, qn_idx, nq_ptr, nq_idx;
@@ -115,6 +117,9 @@ struct PacParams {
   int64_t stride_head;   // elements
   int64_t stride_token;  // elements
   int64_t q_bytes;       // bytes of q ([B][hq][d]); below 2^31 (32-bit gather offsets)
+  const int32_t* page_ptr;  // paged layout: [nodes + 1] (NULL when contiguous)
+  const int32_t* page_idx;  // paged layout: page numbers
+  int32_t page_shift;       // log2(page_size); -1 = contiguous (task tok0 = pool token), else tok0 = position in node
   int32_t num_bins;
   int32_t hq;
   int32_t hkv;

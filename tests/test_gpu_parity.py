@@ -160,6 +160,51 @@ def test_reference_raised_mid_piece(rows):
     check(spec, t, out, lse)
 
 
+# (seed, dtype, kv heads, group, head dim, page size, dot_small, masked fraction, max rows per node)
+PAGED_CASES = [
+    (0, "bf16", 2, 4, 128, 16, False, 0.0, 40),
+    (1, "bf16", 1, 32, 128, 64, False, 0.0, 12),   # many rows: the one-slab-per-wave layout
+    (2, "bf16", 2, 4, 64, 8, False, 0.3, 40),      # head dim 64 (8 tokens per DMA block), masked nodes
+    (3, "f32", 2, 4, 64, 16, False, 0.0, 12),      # float32 dot path
+    (4, "f32", 1, 4, 128, 32, False, 0.3, 12),     # float32, 512-byte rows (2 tokens per DMA block)
+    (5, "bf16", 4, 1, 128, 8, True, 0.3, 40),      # bf16 dot path below 16 rows
+    (6, "bf16", 1, 8, 128, 128, False, 0.0, 40),   # pages longer than a tile
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=[f"paged{c[0]}" for c in PAGED_CASES])
+def test_paged_kv(case):
+    """Paged K/V: pages scattered with holes, page tails and holes filled
+    with NaN (a read past a node's end would poison the output), one spare
+    page per node; the oracle reads the contiguous layout."""
+    seed, dtype, hkv, g, d, P, dot_small, masked, maxq = case
+    spec = workloads.random_tree(2000 + seed, max_nodes=8, max_len=700, max_queries=maxq, num_q_heads=hkv * g,
+                                 num_kv_heads=hkv, head_dim=d, dtype=dtype, masked_prob=masked)
+    say(f"paged case {seed}: page {P} dtype {dtype} H {hkv * g}/{hkv} d {d} N {spec.num_nodes} B {spec.num_queries}")
+    q, k, v = workloads.make_tensors(spec, "cuda")
+    paged, kp, vp = workloads.page_pools(spec, k, v, P, spare_pages=1)
+    tree = pst.Tree.from_paged(spec, paged, out_dtype="f32")
+    plan = pst.Plan(tree, num_bins=5, dot_small=dot_small)
+    out, lse = pst.decode_attn(plan, q, kp, vp)
+    torch.cuda.synchronize()
+    check(spec, (q, k, v), out, lse)
+
+
+@pytest.mark.parametrize("name,P", [("2", 16), ("4", 8)])
+def test_paged_config_sampled(name, P):
+    """A full workload over a paged pool (document QA; masked speculative drafts), sampled queries."""
+    spec = workloads.config(name)
+    q, k, v = workloads.make_tensors(spec, "cuda")
+    paged, kp, vp = workloads.page_pools(spec, k, v, P)
+    say(f"config {name} paged by {P}: {paged['page_ptr'][-1]} pages")
+    tree = pst.Tree.from_paged(spec, paged, out_dtype="f32")
+    plan = pst.Plan(tree)
+    out, lse = pst.decode_attn(plan, q, kp, vp)
+    torch.cuda.synchronize()
+    del kp, vp
+    check(spec, (q, k, v), out, lse, queries=sample(spec.num_queries, 16, 11))
+
+
 def test_max_rows_split():
     """More rows than one workgroup holds: the planner cuts row groups (> 256 rows)."""
     lens = [700] + [3] * 20

@@ -223,3 +223,46 @@ def test_empty_batch():
     p = pst.Plan(t, num_bins=4, host_only=True)
     v = p.view()
     assert v["tasks"].shape == (0, 8) and v["num_slots"] == 0 and p.workspace_bytes == 0
+
+
+def _paged_tree(**kw):
+    base = dict(parent=[-1, 0, 0], kv_len=[20, 9, 3], query_node=[1, 2], page_size=8,
+                page_ptr=[0, 3, 5, 6], page_idx=[7, 2, 9, 0, 4, 11], pool_tokens=0)
+    base.update(kw)
+    return pst.Tree(base["parent"], None, base["kv_len"], base["query_node"], num_q_heads=2, num_kv_heads=1,
+                    head_dim=64, dtype="f32", page_size=base["page_size"], page_ptr=base["page_ptr"],
+                    page_idx=base["page_idx"], pool_tokens=base["pool_tokens"], host_only=True)
+
+
+def test_paged_index_view_and_extent():
+    t = _paged_tree()
+    ix = t.index()
+    assert ix["page_size"] == 8
+    assert ix["page_ptr"].tolist() == [0, 3, 5, 6] and ix["page_idx"].tolist() == [7, 2, 9, 0, 4, 11]
+    assert ix["visible"].tolist() == [29, 23]
+    assert t.kv_extent == 12 * 8 * 64  # (largest page + 1) pages of 8 rows of 64 channels
+    p = pst.Plan(t, num_bins=2, host_only=True)
+    assert p.view()["tasks"].shape[0] == 3  # one piece per node (plan is layout-independent)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(page_size=12), "PST_E_INVALID_ARG"),                  # not a power of two
+    (dict(page_size=4), "PST_E_INVALID_ARG"),                   # below 8 tokens
+    (dict(page_ptr=[1, 3, 5, 6]), "PST_E_INVALID_TREE"),        # page_ptr[0] != 0
+    (dict(page_ptr=[0, 3, 2, 6]), "PST_E_INVALID_TREE"),        # decreasing
+    (dict(page_ptr=[0, 2, 4, 6]), "PST_E_INVALID_TREE"),        # node 0: 20 tokens in 2 pages of 8
+    (dict(page_idx=[7, 2, -1, 0, 4, 11]), "PST_E_INVALID_TREE"),  # negative page
+    (dict(pool_tokens=64), "PST_E_INVALID_TREE"),               # page 11 lies outside 64 rows
+])
+def test_paged_invalid(kw, code):
+    _raises(code, _paged_tree, **kw)
+
+
+def test_paged_growth_within_pages():
+    t = _paged_tree()
+    p = pst.Plan(t, num_bins=2, host_only=True)
+    t.set_lengths([24, 16, 8])  # every node fills its pages exactly
+    assert t.index()["visible"].tolist() == [40, 32]
+    _raises("PST_E_INVALID_TREE", t.set_lengths, [25, 16, 8])  # node 0 would outgrow its 3 pages
+    p.free()
+    t.free()

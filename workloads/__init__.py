@@ -340,3 +340,40 @@ def make_tensors(spec: TreeSpec, device="cpu", *, kv_tokens: Optional[int] = Non
         k[h] = torch.randn((T, d), generator=g, device=dev, dtype=torch.float32).to(dt)
         v[h] = torch.randn((T, d), generator=g, device=dev, dtype=torch.float32).to(dt)
     return q, k, v
+
+
+def page_pools(spec: TreeSpec, k, v, page_size: int, *, spare_pages: int = 0, fill: float = float("nan")):
+    """A paged copy of the contiguous pools ``k``, ``v`` ([H_kv, T, d]).
+
+    Node i gets ceil(kv_len[i] / page_size) + ``spare_pages`` pages.  The
+    physical page numbers are a seeded draw without replacement from a range
+    one eighth larger than needed, so pages are scattered and the pool has
+    holes.  Rows not holding a token (page tails, holes) are set to ``fill``
+    (NaN by default: a read past a node's end poisons the output).  Returns
+    ``({"page_size", "page_ptr", "page_idx"}, k_paged, v_paged)``; token j
+    of node i is row ``page_idx[page_ptr[i] + j // P] * P + j % P``.  The
+    oracle keeps reading the contiguous ``k``, ``v`` with ``spec.kv_offset``.
+    """
+    import torch
+
+    P = int(page_size)
+    kv_len = np.asarray(spec.kv_len, dtype=np.int64)
+    npg = (kv_len + P - 1) // P + int(spare_pages)
+    page_ptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    total = int(page_ptr[-1])
+    rng = np.random.default_rng([spec.seed, 7919, P])
+    page_idx = rng.permutation(total + max(1, total // 8))[:total].astype(np.int32)
+    pool_rows = (int(page_idx.max()) + 1) * P if total else 0
+    src = np.full(pool_rows, -1, dtype=np.int64)  # contiguous row feeding each paged row
+    for i in range(spec.num_nodes):
+        j = np.arange(int(kv_len[i]), dtype=np.int64)
+        pages = page_idx[page_ptr[i]:page_ptr[i + 1]].astype(np.int64)
+        src[pages[j // P] * P + j % P] = int(spec.kv_offset[i]) + j
+    src_t = torch.from_numpy(src).to(k.device)
+    valid = src_t >= 0
+    out = []
+    for x in (k, v):
+        xp = torch.full((x.shape[0], pool_rows, x.shape[2]), fill, dtype=x.dtype, device=x.device)
+        xp[:, valid] = x[:, src_t[valid]]
+        out.append(xp)
+    return {"page_size": P, "page_ptr": page_ptr, "page_idx": page_idx}, out[0], out[1]
