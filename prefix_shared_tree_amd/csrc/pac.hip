@@ -251,24 +251,39 @@ __device__ __forceinline__ void issue_tile(const PacParams& p, const TaskInfo& t
   const int tok_base = tile * G::TT;
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   char* st = pac_lds + stage * STAGE_BYTES;
-  if (p.page_shift >= 0) {
+  constexpr int KB = kHalfOps<NW>;
+  if (p.page_shift >= 0 && (1 << p.page_shift) < G::TT) {
+    // Pages shorter than a tile: consecutive blocks per wavefront, sharing
+    // one page number when a page holds their tokens (see issue_half).
+    const bool shared = (1 << p.page_shift) >= KB * TPB;
+    PagedBlock pw{};
+    if (shared) pw = paged_block(p, t, tok_base, w, KB * TPB);
 #pragma unroll
-    for (int c = 0; c < kHalfOps<NW>; ++c) {
-      const int b = c * NW + w;
-      const PagedBlock pb = paged_block(p, t, tok_base, b, TPB);
+    for (int c = 0; c < KB; ++c) {
+      const int b = KB * w + c;
+      const PagedBlock pb = shared ? pw : paged_block(p, t, tok_base, b, TPB);
+      const int first = shared ? KB * w * TPB : b * TPB;  // first token the descriptor starts at
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(t.kbase + pb.row * stb, pb.valid * stb);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(t.vbase + pb.row * stb, pb.valid * stb);
       const int P = b * 64 + lane;
       const int tok = P / G::CPT, phys = P % G::CPT;
-      const int voff = static_cast<int>((tok - b * TPB) * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4);
+      const int voff = static_cast<int>((tok - first) * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4);
       dma16(rk, voff, lds_addr(st + b * 1024));
       dma16(rv, voff, lds_addr(st + TILE_BYTES + b * 1024));
     }
     return;
   }
+  const char* kb = t.kbase + tok_base * stb;
+  const char* vb = t.vbase + tok_base * stb;
+  if (p.page_shift >= 0) {
+    // Pages of at least a tile: the tile lies in one page.
+    const PagedBlock pb = paged_block(p, t, tok_base, 0, 1);
+    kb = t.kbase + pb.row * stb;
+    vb = t.vbase + pb.row * stb;
+  }
   const int64_t bytes = static_cast<int64_t>(min(G::TT, t.kv_len - tok_base)) * stb;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(t.kbase + tok_base * stb, bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(t.vbase + tok_base * stb, bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, bytes);
 #pragma unroll
   for (int c = 0; c < kHalfOps<NW>; ++c) {
     const int b = c * NW + w;
@@ -339,21 +354,46 @@ __device__ __forceinline__ void issue_half(const PacParams& p, const TaskInfo& t
   constexpr int TPB = 64 / G::CPT;  // tokens per 1 KB block
   const int tok_base = tile * G::TT;
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (p.page_shift >= 0) {
-#pragma unroll
-    for (int c = 0; c < kHalfOps<NW>; ++c) {
-      const int b = c * NW + w;
-      const PagedBlock pb = paged_block(p, t, tok_base, b, TPB);
+  if (p.page_shift >= 0 && (1 << p.page_shift) < G::TT) {
+    // Pages shorter than a tile: this wavefront takes the consecutive blocks
+    // kHalfOps w .. kHalfOps w + kHalfOps - 1, which share one page when a
+    // page holds at least their tokens (one page number and one descriptor),
+    // else each block looks up its own.
+    constexpr int KB = kHalfOps<NW>;
+    if ((1 << p.page_shift) >= KB * TPB) {
+      const PagedBlock pb = paged_block(p, t, tok_base, w, KB * TPB);
       const __amdgpu_buffer_rsrc_t r = make_rsrc(base + pb.row * stb, pb.valid * stb);
-      const int P = b * 64 + lane;
-      const int tok = P / G::CPT, phys = P % G::CPT;
-      dma16(r, static_cast<int>((tok - b * TPB) * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4),
-            lds_addr(dst + b * 1024));
+#pragma unroll
+      for (int c = 0; c < KB; ++c) {
+        const int b = KB * w + c;
+        const int P = b * 64 + lane;
+        const int tok = P / G::CPT, phys = P % G::CPT;
+        dma16(r, static_cast<int>((tok - KB * w * TPB) * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4),
+              lds_addr(dst + b * 1024));
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < KB; ++c) {
+        const int b = KB * w + c;
+        const PagedBlock pb = paged_block(p, t, tok_base, b, TPB);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + pb.row * stb, pb.valid * stb);
+        const int P = b * 64 + lane;
+        const int tok = P / G::CPT, phys = P % G::CPT;
+        dma16(r, static_cast<int>((tok - b * TPB) * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4),
+              lds_addr(dst + b * 1024));
+      }
     }
     return;
   }
+  const char* tbase = base + tok_base * stb;
+  if (p.page_shift >= 0) {
+    // Pages of at least a tile: the tile lies in one page (tiles start at
+    // multiples of 64 tokens of the node), so one page number serves it.
+    const PagedBlock pb = paged_block(p, t, tok_base, 0, 1);
+    tbase = base + pb.row * stb;
+  }
   const int64_t bytes = static_cast<int64_t>(min(G::TT, t.kv_len - tok_base)) * stb;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(base + tok_base * stb, bytes);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(tbase, bytes);
 #pragma unroll
   for (int c = 0; c < kHalfOps<NW>; ++c) {
     const int b = c * NW + w;

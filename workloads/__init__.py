@@ -342,14 +342,16 @@ def make_tensors(spec: TreeSpec, device="cpu", *, kv_tokens: Optional[int] = Non
     return q, k, v
 
 
-def page_pools(spec: TreeSpec, k, v, page_size: int, *, spare_pages: int = 0, fill: float = float("nan")):
+def page_pools(spec: TreeSpec, k, v, page_size: int, *, spare_pages: int = 0, fill: float = float("nan"),
+               scatter: bool = True):
     """A paged copy of the contiguous pools ``k``, ``v`` ([H_kv, T, d]).
 
     Node i gets ceil(kv_len[i] / page_size) + ``spare_pages`` pages.  The
     physical page numbers are a seeded draw without replacement from a range
     one eighth larger than needed, so pages are scattered and the pool has
     holes.  Rows not holding a token (page tails, holes) are set to ``fill``
-    (NaN by default: a read past a node's end poisons the output).  Returns
+    (NaN by default: a read past a node's end poisons the output).  With
+    ``scatter`` False the pages are numbered in order without holes.  Returns
     ``({"page_size", "page_ptr", "page_idx"}, k_paged, v_paged)``; token j
     of node i is row ``page_idx[page_ptr[i] + j // P] * P + j % P``.  The
     oracle keeps reading the contiguous ``k``, ``v`` with ``spec.kv_offset``.
@@ -362,7 +364,10 @@ def page_pools(spec: TreeSpec, k, v, page_size: int, *, spare_pages: int = 0, fi
     page_ptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
     total = int(page_ptr[-1])
     rng = np.random.default_rng([spec.seed, 7919, P])
-    page_idx = rng.permutation(total + max(1, total // 8))[:total].astype(np.int32)
+    if scatter:
+        page_idx = rng.permutation(total + max(1, total // 8))[:total].astype(np.int32)
+    else:
+        page_idx = np.arange(total, dtype=np.int32)
     pool_rows = (int(page_idx.max()) + 1) * P if total else 0
     src = np.full(pool_rows, -1, dtype=np.int64)  # contiguous row feeding each paged row
     for i in range(spec.num_nodes):
