@@ -1110,10 +1110,14 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
   }
 }
 
-template <typename T, int D>
+// PAGED selects the instantiation for the paged K/V layout; the contiguous
+// one is compiled without the page-table code (its registers and scalar
+// registers stay with the tile loop).
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kWaves<T> * 64) __attribute__((amdgpu_waves_per_eu(kWaves<T> / 4, kWaves<T> / 4)))
 void pac_kernel(PacParams p) {
   constexpr int NW = kWaves<T>;
+  if constexpr (!PAGED) p.page_shift = -1;  // every page-table branch folds away
   const int bin = blockIdx.x % p.num_bins;
   const int kvh = blockIdx.x / p.num_bins;
   const int tb = p.bin_ptr[bin], te = p.bin_ptr[bin + 1];
@@ -1170,19 +1174,23 @@ void pac_kernel(PacParams p) {
   }
 }
 
-template <typename T, int D>
-int launch_one(const PacParams& p, void* stream) {
+template <typename T, int D, bool PAGED>
+int launch_layout(const PacParams& p, void* stream) {
   const int grid = p.num_bins * p.hkv;
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pac_kernel<T, D>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pac_kernel<T, D, PAGED>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
     if (e != hipSuccess) return static_cast<int>(e);
     configured = true;
   }
-  hipLaunchKernelGGL((pac_kernel<T, D>), dim3(grid), dim3(kWaves<T> * 64), kLdsBytes, static_cast<hipStream_t>(stream),
-                     p);
+  hipLaunchKernelGGL((pac_kernel<T, D, PAGED>), dim3(grid), dim3(kWaves<T> * 64), kLdsBytes,
+                     static_cast<hipStream_t>(stream), p);
   return static_cast<int>(hipGetLastError());
+}
+template <typename T, int D>
+int launch_one(const PacParams& p, void* stream) {
+  return p.page_shift >= 0 ? launch_layout<T, D, true>(p, stream) : launch_layout<T, D, false>(p, stream);
 }
 
 }  // namespace
@@ -1198,13 +1206,13 @@ int launch_pac(const PacParams& p, int in_dtype, int head_dim, void* stream) {
 int pac_blocks_per_cu(int in_dtype, int head_dim, int* blocks) {
   hipError_t e;
   if (in_dtype == PST_BF16 && head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 128>, kWaves<uint16_t> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 128, false>, kWaves<uint16_t> * 64, kLdsBytes);
   else if (in_dtype == PST_BF16)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 64>, kWaves<uint16_t> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 64, false>, kWaves<uint16_t> * 64, kLdsBytes);
   else if (head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 128>, kWaves<float> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 128, false>, kWaves<float> * 64, kLdsBytes);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 64>, kWaves<float> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 64, false>, kWaves<float> * 64, kLdsBytes);
   return static_cast<int>(e);
 }
 
