@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the warm-cache timing (every PAC launch of the run is then cold, as under a profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--decode-steps", type=int, default=0,
+                    help="> 0: time a decode loop of this many steps (one token appended to every query's leaf per "
+                         "step, paged pool) with the plan reused, re-planned every 16 steps and every step")
     ap.add_argument("--page-size", type=int, default=0,
                     help="> 0: K/V in a paged pool of pages of this many tokens (scattered, with holes)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "pac_traffic.json"),
@@ -145,6 +148,57 @@ def cpu_baseline(spec, q, k, v, out, budget_s):
     }
 
 
+def decode_loop_bench(torch, pst, workloads, spec, a):
+    """Multi-step decoding: per step, append one token to every query's leaf
+    and run PAC + POR; wall time per step includes the host length update
+    (and re-planning when due).  The same new K/V rows and queries feed
+    every policy."""
+    from prefix_shared_tree_amd.decode_loop import DecodeSession
+
+    S = a.decode_steps
+    P = a.page_size if a.page_size > 0 else 16
+    print(f"[bench] decode loop on {spec.name}: {S} steps, {P}-token pages", file=sys.stderr, flush=True)
+    q, k, v = workloads.make_tensors(spec, "cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2024)
+    B, hkv, hq, d = spec.num_queries, spec.num_kv_heads, spec.num_q_heads, spec.head_dim
+    dt = q.dtype
+    kn = torch.randn((S, B, hkv, d), generator=g, device="cuda").to(dt)
+    vn = torch.randn((S, B, hkv, d), generator=g, device="cuda").to(dt)
+    qs = torch.randn((S, B, hq, d), generator=g, device="cuda").to(dt)
+    out = torch.empty((B, hq, d), device="cuda", dtype=torch.float32)
+    lse = torch.empty((B, hq), device="cuda", dtype=torch.float32)
+    results = {}
+    for name, every in (("reuse", 0), ("replan_every_16", 16), ("replan_every_step", 1)):
+        sess = DecodeSession(spec, k, v, page_size=P, max_new_tokens=S, replan_every=every)
+        torch.cuda.synchronize()
+        gpu = []
+        t0 = time.perf_counter()
+        for s in range(S):
+            sess.append(kn[s], vn[s])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            sess.decode(qs[s], out=out, lse=lse)
+            e1.record()
+            gpu.append((e0, e1))
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / S
+        results[name] = {
+            "wall_ms_per_step": wall * 1e3,
+            "gpu_ms_per_step": statistics.mean(x.elapsed_time(y) for x, y in gpu),
+            "replans": sess.replans,
+            "replan_ms_each": sess.replan_s * 1e3 / sess.replans if sess.replans else 0.0,
+        }
+        del sess
+    print(json.dumps({
+        "metric": "decode steps/s (append one token per query, PAC + POR, host length update and re-planning)",
+        "value": 1e3 / results["reuse"]["wall_ms_per_step"], "unit": "steps/s", "n_gpus": 1, "steps": S,
+        "higher_is_better": True, "dtype": spec.dtype, "data": "synthetic",
+        "config": {"workload": spec.name, "kv_layout": f"paged, {P}-token pages", "mode": "decode_loop"},
+        "policies": results,
+    }))
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -157,6 +211,9 @@ def main():
     import workloads
 
     spec = workloads.config(a.config)
+    if a.decode_steps > 0:
+        decode_loop_bench(torch, pst, workloads, spec, a)
+        return
     print(f"[bench] workload {spec.name}: generating inputs", file=sys.stderr, flush=True)
     q, k, v = workloads.make_tensors(spec, "cuda")
     # The kernels read kk, vv (the contiguous pools, or a paged copy); the

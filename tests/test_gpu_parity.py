@@ -306,3 +306,41 @@ def test_workspace_errors():
     with pytest.raises(pst.PstError) as e:
         pst.decode_attn(plan, q, k, v, ws=small)
     assert e.value.code == "PST_E_WORKSPACE"
+
+
+@pytest.mark.parametrize("replan_every", [0, 2])
+def test_decode_session_steps(replan_every):
+    """Multi-step decoding: each step appends one token to every query's leaf
+    (paged pool, plan reused through pst_tree_set_lengths, or re-planned every
+    second step) and is checked against the oracle on a contiguous mirror."""
+    from prefix_shared_tree_amd.decode_loop import DecodeSession
+
+    parent = np.array([-1, 0, 0, 0, 1, 1, 2, 2, 3, 3])
+    lens = np.array([700, 100, 37, 64, 40, 1, 63, 16, 9, 70])
+    qnode = np.array([4, 5, 6, 7, 8, 9])
+    steps = 6
+    cap = lens.copy()
+    cap[qnode] += steps
+    off = np.concatenate([[0], np.cumsum(cap)[:-1]])
+    spec0 = workloads.TreeSpec("decode", parent, lens, off, qnode, 16, 4, 128, "bf16", 91)
+    q, k, v = workloads.make_tensors(spec0, "cuda", kv_tokens=int(cap.sum()))
+    sess = DecodeSession(spec0, k, v, page_size=16, max_new_tokens=steps, replan_every=replan_every,
+                         plan_kw=dict(num_bins=3))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242 + replan_every)
+    cur = lens.copy()
+    for s in range(steps):
+        kn = torch.randn((len(qnode), 4, 128), generator=g, device="cuda").to(torch.bfloat16)
+        vn = torch.randn((len(qnode), 4, 128), generator=g, device="cuda").to(torch.bfloat16)
+        sess.append(kn, vn)
+        rows = torch.from_numpy(off[qnode] + cur[qnode]).cuda()
+        k[:, rows] = kn.transpose(0, 1)
+        v[:, rows] = vn.transpose(0, 1)
+        cur[qnode] += 1
+        spec = workloads.TreeSpec("decode", parent, cur, off, qnode, 16, 4, 128, "bf16", 91)
+        qs = torch.randn((len(qnode), 16, 128), generator=g, device="cuda").to(torch.bfloat16)
+        out, lse = sess.decode(qs)
+        torch.cuda.synchronize()
+        say(f"step {s + 1}: lengths {cur[qnode].tolist()}, replans {sess.replans}")
+        check(spec, (qs, k, v), out, lse)
+    assert sess.replans == (steps // replan_every if replan_every else 0)
