@@ -332,12 +332,18 @@ def main():
 
 
 def kernel_sha():
+    """Hash of the PAC kernel's code (comments and blank lines removed, so a
+    comment edit keeps the recorded traffic; any code change drops it)."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for name in ("pac.hip", "pst_internal.h"):
-        with open(os.path.join(ROOT, "prefix_shared_tree_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "prefix_shared_tree_amd", "csrc", name), encoding="utf-8") as f:
+            for line in f:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

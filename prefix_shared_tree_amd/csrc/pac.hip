@@ -20,7 +20,9 @@
 // (buffer_load_dwordx4 ... lds), four stages deep, so three tiles are in
 // flight while one is computed and no registers hold staged data.  Rows are
 // XOR-swizzled by 16-byte chunk so the reads below spread over the banks;
-// loads past the piece end return zeros.
+// loads past the piece end return zeros.  Paged K/V (a node as a list of
+// pages of a paged pool) is a separate instantiation: each DMA block finds
+// its page through the page table (one scalar read per page run).
 //
 // Two compute paths, chosen per piece:
 //  * matrix cores (every bf16 piece by default): each wavefront owns 16 or 32
@@ -29,9 +31,11 @@
 //    so every row's softmax state stays in one lane.  V^T fragments come
 //    straight from the row-major tile with the LDS transpose read
 //    ds_read_b64_tr_b16.  The product O += P V of a tile runs one tile late,
-//    next to the next tile's softmax, so matrix cores and vector ALU overlap;
-//    for it each V tile is converted once in LDS to fp16 (scaled by 2^-8) and
-//    P is rounded to fp16;
+//    next to the next tile's softmax; for it each V tile is converted once in
+//    LDS to fp16 (scaled by 2^-8) and P is rounded to fp16.  Layouts with two
+//    wavefronts per slab (up to 128 rows, bandwidth-bound) interleave products
+//    and softmax; one slab per wavefront (more rows, compute-bound) issues a
+//    step's products first and tests the lazy maximum per lane;
 //  * wavefront dot products (float32, or bf16 pieces below 16 rows on
 //    request): groups of head_dim*elem/16 lanes take one token each, reduce
 //    q.k across the group with DPP, and keep a running (max, sum, O) per row;
