@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=0,
                     help="> 0: time a decode loop of this many steps (one token appended to every query's leaf per "
                          "step, paged pool) with the plan reused, re-planned every 16 steps and every step")
+    ap.add_argument("--sweep", action="store_true",
+                    help="tree-shape sweep (2T..5T k-ary trees and a degenerate tree; CoDec's shapes): tree path, "
+                         "tree path without splitting, and the query-guided baseline per shape")
     ap.add_argument("--page-size", type=int, default=0,
                     help="> 0: K/V in a paged pool of pages of this many tokens (scattered, with holes)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "pac_traffic.json"),
@@ -148,6 +151,47 @@ def cpu_baseline(spec, q, k, v, out, budget_s):
     }
 
 
+def shape_sweep(torch, pst, workloads, a):
+    """CoDec's tree shapes (binary .. 5-ary trees, a degenerate tree), 4096
+    tokens per query path, half of them in the shared root, GQA 32/8, d 128,
+    bf16.  Per shape, cold-cache PAC + POR of: the tree path; the tree path
+    with every node one piece (no workload partitioning); the query-guided
+    (FlashDecoding-style) baseline, which reads shared KV once per query."""
+    shapes = [workloads.kary_tree(2, 7), workloads.kary_tree(3, 5), workloads.kary_tree(4, 4),
+              workloads.kary_tree(5, 4), workloads.degenerate_tree(64)]
+    evict_bufs = (torch.empty(1 << 30, dtype=torch.uint8, device="cuda"),
+                  torch.empty(4096, dtype=torch.float32, device="cuda"))
+    rows = {}
+    for spec in shapes:
+        print(f"[bench] shape {spec.name}", file=sys.stderr, flush=True)
+        q, k, v = workloads.make_tensors(spec, "cuda")
+        tree = pst.Tree.from_spec(spec, out_dtype="f32")
+        st = workload_stats(spec, tree)
+        out = torch.empty((spec.num_queries, spec.num_q_heads, spec.head_dim), device="cuda", dtype=torch.float32)
+        lse = torch.empty((spec.num_queries, spec.num_q_heads), device="cuda", dtype=torch.float32)
+        r = {"nodes": spec.num_nodes, "queries": spec.num_queries, "unique_kv_bytes": st["unique_kv_bytes"],
+             "per_query_kv_bytes": st["per_query_kv_bytes"],
+             "kv_read_ratio": st["per_query_kv_bytes"] / st["unique_kv_bytes"]}
+        for name, kw in (("tree", {}), ("tree_no_split", {"no_split": True}), ("query_guided", {"query_guided": True})):
+            plan = pst.Plan(tree, **kw)
+            ws = pst.workspace(plan)
+            pac, por, _ = time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, a.steps, a.warmup)
+            r[name + "_ms"] = statistics.mean(x + y for x, y in zip(pac, por))
+            del ws, plan
+        r["speedup_over_query_guided"] = r["query_guided_ms"] / r["tree_ms"]
+        r["speedup_of_partitioning"] = r["tree_no_split_ms"] / r["tree_ms"]
+        r["unique_kv_frac_of_peak"] = st["unique_kv_bytes"] / (r["tree_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS
+        rows[spec.name] = r
+        del q, k, v, tree
+    print(json.dumps({
+        "metric": "tree-shape sweep: PAC + POR ms per shape, tree path vs query-guided baseline",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "higher_is_better": False, "dtype": "bf16",
+        "data": "synthetic", "config": {"mode": "shape_sweep", "path_len": 4096, "shared_root": 0.5,
+                                         "heads": "32/8", "head_dim": 128},
+        "shapes": rows,
+    }))
+
+
 def decode_loop_bench(torch, pst, workloads, spec, a):
     """Multi-step decoding: per step, append one token to every query's leaf
     and run PAC + POR; wall time per step includes the host length update
@@ -210,6 +254,9 @@ def main():
     import prefix_shared_tree_amd as pst
     import workloads
 
+    if a.sweep:
+        shape_sweep(torch, pst, workloads, a)
+        return
     spec = workloads.config(a.config)
     if a.decode_steps > 0:
         decode_loop_bench(torch, pst, workloads, spec, a)

@@ -382,3 +382,51 @@ def page_pools(spec: TreeSpec, k, v, page_size: int, *, spare_pages: int = 0, fi
         xp[:, valid] = x[:, src_t[valid]]
         out.append(xp)
     return {"page_size": P, "page_ptr": page_ptr, "page_idx": page_idx}, out[0], out[1]
+
+
+# ---------------------------------------------------------------------------
+# Tree shapes of the CoDec evaluation (binary 2T ... 5-ary 5T and a degenerate
+# tree DT; CoDec page, 实验结果 section 1).  The page names the shapes and
+# sweeps sequence length, batch and shared-prefix ratio without printing the
+# trees, so the sizes below are this build's reading: every query's path holds
+# `path_len` tokens, the root `shared` of them, the rest split evenly over
+# the deeper levels; one query per leaf.
+# ---------------------------------------------------------------------------
+
+def kary_tree(k: int, depth: int, *, path_len: int = 4096, shared: float = 0.5, num_q_heads: int = 32,
+              num_kv_heads: int = 8, head_dim: int = 128, dtype: str = "bf16", seed: int = 7) -> TreeSpec:
+    """Full k-ary tree of `depth` levels (k^(depth-1) leaves, one query each)."""
+    root = int(round(path_len * shared))
+    per = max(1, (path_len - root) // max(1, depth - 1))
+    parent, lens, level = [-1], [root], [0]
+    for lv in range(1, depth):
+        for p in [i for i, d in enumerate(level) if d == lv - 1]:
+            for _ in range(k):
+                parent.append(p)
+                lens.append(per)
+                level.append(lv)
+    leaves = np.array([i for i, d in enumerate(level) if d == depth - 1], dtype=np.int32)
+    return TreeSpec(f"{k}T-depth{depth}", np.array(parent), np.array(lens), _offsets(lens), leaves,
+                    num_q_heads, num_kv_heads, head_dim, dtype, seed)
+
+
+def degenerate_tree(queries: int, *, path_len: int = 4096, shared: float = 0.5, num_q_heads: int = 32,
+                    num_kv_heads: int = 8, head_dim: int = 128, dtype: str = "bf16", seed: int = 7) -> TreeSpec:
+    """Degenerate tree DT: a chain of `queries` nodes below the root, each with
+    a leaf hanging off it, so query i shares the root and i chain nodes with
+    the others and prefixes vary from shared to nearly private.  The chain
+    splits the unshared part of the longest path evenly; every leaf tops its
+    path up to `path_len` tokens."""
+    root = int(round(path_len * shared))
+    step = max(1, (path_len - root) // (queries + 1))
+    parent, lens, leaves = [-1], [root], []
+    chain = 0
+    for i in range(queries):
+        parent.append(chain)  # next chain node
+        lens.append(step)
+        chain = len(parent) - 1
+        parent.append(chain)  # leaf of query i
+        lens.append(max(1, path_len - root - (i + 1) * step))
+        leaves.append(len(parent) - 1)
+    return TreeSpec(f"DT-{queries}", np.array(parent), np.array(lens), _offsets(lens), np.array(leaves),
+                    num_q_heads, num_kv_heads, head_dim, dtype, seed)
