@@ -234,6 +234,34 @@ def decode_loop_bench(torch, pst, workloads, spec, a):
             "replan_ms_each": sess.replan_s * 1e3 / sess.replans if sess.replans else 0.0,
         }
         del sess
+    # Tree search: every 8 steps one query finishes and another forks in two,
+    # so the batch keeps its size; each fork or finish rebuilds tree and plan.
+    per = -(-(1 + S) // P)
+    sess = DecodeSession(spec, k, v, page_size=P, max_new_tokens=S, extra_pages=per * (2 * (S // 8) + 2))
+    torch.cuda.synchronize()
+    gpu, topo = [], []
+    t0 = time.perf_counter()
+    for s in range(S):
+        if s and s % 8 == 0:
+            t1 = time.perf_counter()
+            sess.prune(0)
+            sess.branch(sess.num_queries - 1, kn[s][:2], vn[s][:2])
+            torch.cuda.synchronize()
+            topo.append(time.perf_counter() - t1)
+        sess.append(kn[s], vn[s])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        sess.decode(qs[s], out=out, lse=lse)
+        e1.record()
+        gpu.append((e0, e1))
+    torch.cuda.synchronize()
+    results["search_fork_finish_every_8"] = {
+        "wall_ms_per_step": (time.perf_counter() - t0) * 1e3 / S,
+        "gpu_ms_per_step": statistics.mean(x.elapsed_time(y) for x, y in gpu),
+        "rebuilds": 2 * len(topo),
+        "finish_plus_fork_ms_each": statistics.mean(topo) * 1e3 if topo else 0.0,
+    }
+    del sess
     print(json.dumps({
         "metric": "decode steps/s (append one token per query, PAC + POR, host length update and re-planning)",
         "value": 1e3 / results["reuse"]["wall_ms_per_step"], "unit": "steps/s", "n_gpus": 1, "steps": S,

@@ -310,7 +310,12 @@ def default_cost_model(head_dim: int, num_q_heads: int, num_kv_heads: int, dtype
     """The fitted gfx950 table shipped for this head layout, if there is one."""
     name = f"gfx950_{'bf16' if _dtype_code(dtype) == PST_BF16 else 'f32'}_q{num_q_heads}_kv{num_kv_heads}_d{head_dim}.json"
     path = os.path.join(_HERE, "cost_tables", name)
-    return CostModel.load(path) if os.path.exists(path) else None
+    if path not in _COST_CACHE:
+        _COST_CACHE[path] = CostModel.load(path) if os.path.exists(path) else None
+    return _COST_CACHE[path]
+
+
+_COST_CACHE: dict = {}  # fitted tables by path (read-only once loaded)
 
 
 class Plan:

@@ -35,33 +35,57 @@ static pst_status hip_fail(const char* what, hipError_t e) {
   return PST_E_HIP;
 }
 
-template <typename T>
-static pst_status dev_upload(T** dst, const T* src, size_t count, hipStream_t s) {
-  *dst = nullptr;
-  const size_t bytes = std::max<size_t>(count, 1) * sizeof(T);
-  if (inject_alloc_failure()) {
-    set_error("injected device allocation failure");
-    return PST_E_OOM;
+// One device allocation per object: every array sits at a 256-byte aligned
+// offset and arrives with one host-to-device copy from a packed staging
+// buffer (a tree or plan rebuilt per topology change then costs one
+// allocation, one copy and one free instead of one of each per array).
+class DevArena {
+ public:
+  template <typename T>
+  void add(T** dst, const T* src, size_t count) {
+    parts_.push_back({reinterpret_cast<void**>(dst), src, count * sizeof(T), size_});
+    size_ += (std::max<size_t>(count * sizeof(T), 1) + 255) & ~static_cast<size_t>(255);
   }
-  hipError_t e = hipMalloc(reinterpret_cast<void**>(dst), bytes);
-  if (e != hipSuccess) {
-    *dst = nullptr;
-    (void)hipGetLastError();
-    set_error(std::string("hipMalloc failed: ") + hipGetErrorString(e));
-    return PST_E_OOM;
+  // Allocates, copies on stream s and waits for the copy (the staging buffer
+  // is freed on return).  On failure *base stays null.
+  pst_status commit(void** base, hipStream_t s) {
+    *base = nullptr;
+    if (inject_alloc_failure()) {
+      set_error("injected device allocation failure");
+      return PST_E_OOM;
+    }
+    hipError_t e = hipMalloc(base, size_);
+    if (e != hipSuccess) {
+      *base = nullptr;
+      (void)hipGetLastError();
+      set_error(std::string("hipMalloc failed: ") + hipGetErrorString(e));
+      return PST_E_OOM;
+    }
+    std::vector<char> staging(size_, 0);
+    for (const Part& a : parts_) {
+      if (a.bytes) std::memcpy(staging.data() + a.offset, a.src, a.bytes);
+      *a.dst = static_cast<char*>(*base) + a.offset;
+    }
+    e = hipMemcpyAsync(*base, staging.data(), size_, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      for (const Part& a : parts_) *a.dst = nullptr;
+      (void)hipFree(*base);
+      *base = nullptr;
+      return hip_fail("upload", e);
+    }
+    return PST_OK;
   }
-  if (count) {
-    e = hipMemcpyAsync(*dst, src, count * sizeof(T), hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return hip_fail("hipMemcpyAsync", e);
-  }
-  return PST_OK;
-}
 
-template <typename T>
-static void dev_free(T*& p) {
-  if (p) (void)hipFree(p);
-  p = nullptr;
-}
+ private:
+  struct Part {
+    void** dst;
+    const void* src;
+    size_t bytes, offset;
+  };
+  std::vector<Part> parts_;
+  size_t size_ = 0;
+};
 
 }  // namespace pst
 
@@ -77,6 +101,7 @@ struct pst_tree_s {
   uint64_t generation = 0;  // bumped when the device index is rebuilt
   int live_plans = 0;
   std::vector<pst_plan_s*> plans;  // live plans: their device tasks follow length changes
+  void* d_arena = nullptr;  // holds every d_ array below
   int64_t* d_node_off = nullptr;
   int32_t* d_node_len = nullptr;
   int32_t* d_page_ptr = nullptr;
@@ -94,6 +119,7 @@ struct pst_plan_s {
   PlanOptions opts;
   PlanResult r;
   bool on_device = false;
+  void* d_arena = nullptr;  // holds every d_ array below
   DevTask* d_tasks = nullptr;
   int32_t* d_bin_ptr = nullptr;
   int32_t* d_entry_slot = nullptr;
@@ -107,22 +133,23 @@ struct pst_cost_s {
 };
 
 static void free_tree_device(pst_tree_s* t) {
-  dev_free(t->d_node_off);
-  dev_free(t->d_node_len);
-  dev_free(t->d_page_ptr);
-  dev_free(t->d_page_idx);
-  dev_free(t->d_node_masked);
-  dev_free(t->d_nq_ptr);
-  dev_free(t->d_nq_idx);
-  dev_free(t->d_nq_mask);
+  if (t->d_arena) (void)hipFree(t->d_arena);
+  t->d_arena = nullptr;
+  t->d_node_off = nullptr;
+  t->d_node_len = nullptr;
+  t->d_page_ptr = t->d_page_idx = nullptr;
+  t->d_node_masked = nullptr;
+  t->d_nq_ptr = t->d_nq_idx = nullptr;
+  t->d_nq_mask = nullptr;
   t->on_device = false;
 }
 
 static void free_plan_device(pst_plan_s* p) {
-  dev_free(p->d_tasks);
-  dev_free(p->d_bin_ptr);
-  dev_free(p->d_entry_slot);
-  dev_free(p->d_slot_ptr);
+  if (p->d_arena) (void)hipFree(p->d_arena);
+  p->d_arena = nullptr;
+  p->d_tasks = nullptr;
+  p->d_bin_ptr = p->d_entry_slot = nullptr;
+  p->d_slot_ptr = nullptr;
   p->on_device = false;
 }
 
@@ -220,19 +247,18 @@ pst_status pst_tree_build(const pst_tree_desc* desc, const pst_shape* shape, uin
       return PST_E_NO_DEVICE;
     }
     const TreeIndex& ix = t->ix;
-    st = dev_upload(&t->d_node_off, ix.kv_offset.data(), ix.N, s);
-    if (st == PST_OK) st = dev_upload(&t->d_node_len, ix.kv_len.data(), ix.N, s);
-    if (st == PST_OK && ix.page_size > 0) st = dev_upload(&t->d_page_ptr, ix.page_ptr.data(), ix.page_ptr.size(), s);
-    if (st == PST_OK && ix.page_size > 0 && !ix.page_idx.empty())
-      st = dev_upload(&t->d_page_idx, ix.page_idx.data(), ix.page_idx.size(), s);
-    if (st == PST_OK) st = dev_upload(&t->d_node_masked, ix.masked.data(), ix.N, s);
-    if (st == PST_OK) st = dev_upload(&t->d_nq_ptr, ix.nq_ptr.data(), ix.nq_ptr.size(), s);
-    if (st == PST_OK) st = dev_upload(&t->d_nq_idx, ix.nq_idx.data(), ix.nq_idx.size(), s);
-    if (st == PST_OK) st = dev_upload(&t->d_nq_mask, ix.nq_mask.data(), ix.nq_mask.size(), s);
-    if (st == PST_OK) {
-      e = hipStreamSynchronize(s);
-      if (e != hipSuccess) st = hip_fail("hipStreamSynchronize", e);
+    DevArena arena;
+    arena.add(&t->d_node_off, ix.kv_offset.data(), ix.N);
+    arena.add(&t->d_node_len, ix.kv_len.data(), ix.N);
+    if (ix.page_size > 0) {
+      arena.add(&t->d_page_ptr, ix.page_ptr.data(), ix.page_ptr.size());
+      arena.add(&t->d_page_idx, ix.page_idx.data(), ix.page_idx.size());
     }
+    arena.add(&t->d_node_masked, ix.masked.data(), ix.N);
+    arena.add(&t->d_nq_ptr, ix.nq_ptr.data(), ix.nq_ptr.size());
+    arena.add(&t->d_nq_idx, ix.nq_idx.data(), ix.nq_idx.size());
+    arena.add(&t->d_nq_mask, ix.nq_mask.data(), ix.nq_mask.size());
+    st = arena.commit(&t->d_arena, s);
     if (st != PST_OK) {
       free_tree_device(t);
       delete t;
@@ -499,14 +525,12 @@ pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* op
       b.flags = ((a.flags & PST_TASK_LAST_PIECE) ? kDevLast : 0) | (t->ix.masked[a.node] ? kDevMasked : 0);
       b.reserved = 0;
     }
-    st = dev_upload(&p->d_tasks, dt.data(), dt.size(), s);
-    if (st == PST_OK) st = dev_upload(&p->d_bin_ptr, p->r.bin_ptr.data(), p->r.bin_ptr.size(), s);
-    if (st == PST_OK) st = dev_upload(&p->d_entry_slot, es32.data(), es32.size(), s);
-    if (st == PST_OK) st = dev_upload(&p->d_slot_ptr, p->r.slot_ptr.data(), p->r.slot_ptr.size(), s);
-    if (st == PST_OK) {
-      hipError_t e = hipStreamSynchronize(s);
-      if (e != hipSuccess) st = hip_fail("hipStreamSynchronize", e);
-    }
+    DevArena arena;
+    arena.add(&p->d_tasks, dt.data(), dt.size());
+    arena.add(&p->d_bin_ptr, p->r.bin_ptr.data(), p->r.bin_ptr.size());
+    arena.add(&p->d_entry_slot, es32.data(), es32.size());
+    arena.add(&p->d_slot_ptr, p->r.slot_ptr.data(), p->r.slot_ptr.size());
+    st = arena.commit(&p->d_arena, s);
     if (st != PST_OK) {
       free_plan_device(p);
       delete p;

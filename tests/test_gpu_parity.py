@@ -344,3 +344,40 @@ def test_decode_session_steps(replan_every):
         say(f"step {s + 1}: lengths {cur[qnode].tolist()}, replans {sess.replans}")
         check(spec, (qs, k, v), out, lse)
     assert sess.replans == (steps // replan_every if replan_every else 0)
+
+
+@pytest.mark.gpu
+def test_decode_session_branch_prune():
+    """Tree search over a paged pool: queries grow, fork and finish; after every
+    change each query's attention is checked against the oracle on the tree the
+    session holds, gathered back to the contiguous layout."""
+    from prefix_shared_tree_amd.decode_loop import DecodeSession
+
+    parent = np.array([-1, 0, 0, 1])
+    lens = np.array([900, 130, 7, 64])
+    off = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    spec0 = workloads.TreeSpec("search", parent, lens, off, np.array([2, 3]), 16, 4, 128, "bf16", 17)
+    q, k, v = workloads.make_tensors(spec0, "cuda")
+    sess = DecodeSession(spec0, k, v, page_size=16, max_new_tokens=8, extra_pages=80, plan_kw=dict(num_bins=5))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+
+    def rows(n):
+        return torch.randn((n, 4, 128), generator=g, device="cuda").to(torch.bfloat16)
+
+    for op in ["a", "b3", "a", "b2", "a", "p1", "a", "b1", "p0", "a", "p2"]:
+        if op == "a":
+            B = sess.num_queries
+            sess.append(rows(B), rows(B))
+        elif op[0] == "b":
+            n = int(op[1])
+            sess.branch(sess.num_queries - 1, rows(n), rows(n))
+        else:
+            sess.prune(int(op[1]))
+        parent, kv_len, koff, qn, kc, vc = sess.contiguous()
+        spec = workloads.TreeSpec("search", parent, kv_len, koff, qn, 16, 4, 128, "bf16", 17)
+        qs = torch.randn((sess.num_queries, 16, 128), generator=g, device="cuda").to(torch.bfloat16)
+        out, lse = sess.decode(qs)
+        torch.cuda.synchronize()
+        say(f"{op}: {sess.num_queries} queries, {len(kv_len)} nodes, {len(sess.free)} free pages")
+        check(spec, (qs, kc, vc), out, lse)

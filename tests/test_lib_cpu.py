@@ -266,3 +266,120 @@ def test_paged_growth_within_pages():
     _raises("PST_E_INVALID_TREE", t.set_lengths, [25, 16, 8])  # node 0 would outgrow its 3 pages
     p.free()
     t.free()
+
+
+def _session_model_check(sess, nodes, queries, P, cm, planned=True):
+    """The session against a plain model: ``nodes`` is a list of [parent, token ids, alive]
+    (never reordered), ``queries`` the model node of each query.  ``planned``: the plan was
+    made for the current lengths (else it is the one made before the last growth)."""
+    import torch
+
+    alive = [i for i, n in enumerate(nodes) if n[2]]
+    rank = {m: r for r, m in enumerate(alive)}
+    par = [rank[nodes[m][0]] if nodes[m][0] >= 0 else -1 for m in alive]
+    assert sess.parent.tolist() == par
+    assert sess.kv_len.tolist() == [len(nodes[m][1]) for m in alive]
+    assert sess.query_node.tolist() == [rank[m] for m in queries]
+    # Pages: live nodes own disjoint pages that, with the free list, cover the pool once.
+    owned = [p for pg in sess.pages for p in pg]
+    assert sorted(owned + sess.free) == list(range(sess.pool_pages))
+    for i, m in enumerate(alive):
+        assert len(sess.pages[i]) * P >= len(nodes[m][1])
+    # Every token sits in the pool where the page table says.
+    parent, kv_len, off, qn, k, v = sess.contiguous()
+    want = [t for m in alive for t in nodes[m][1]]
+    assert k[0, :, 0].tolist() == want and v[1, :, 3].tolist() == [-t for t in want]
+    # Index and plan of the rebuilt tree, bit-exact against the oracle.
+    spec = workloads.TreeSpec("session", parent, kv_len, off, qn, 4, 2, 64, "f32", 0)
+    ix = oracle.build_index(spec)
+    got = sess.tree.index()
+    for key in ix:
+        assert np.array_equal(got[key], ix[key].astype(got[key].dtype)), key
+    paths = []
+    for m in queries:
+        s, n = 0, m
+        while n >= 0:
+            s += len(nodes[n][1])
+            n = nodes[n][0]
+        paths.append(s)
+    assert got["visible"].tolist() == paths
+    if planned:
+        sess._planned_lens = kv_len
+    spec.kv_len = sess._planned_lens
+    want_plan = oracle.plan(oracle.build_index(spec), sess._planned_lens, spec.group, cm, 5, r_max=16)
+    assert np.array_equal(sess.plan.view()["tasks"][:, :7], want_plan["tasks"])
+
+
+def test_decode_session_branch_prune_bookkeeping():
+    """Append, branch and prune on a host-only session: the tree, the page
+    pool and the plan stay consistent with a model that never moves nodes."""
+    import torch
+
+    from prefix_shared_tree_amd.decode_loop import DecodeSession
+
+    P, max_new = 8, 24
+    parent = np.array([-1, 0, 0, 1])
+    lens = np.array([40, 17, 5, 9])
+    off = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    qnode = np.array([2, 3])
+    spec = workloads.TreeSpec("session", parent, lens, off, qnode, 4, 2, 64, "f32", 0)
+    T = int(lens.sum())
+    ids = torch.arange(1, T + 1, dtype=torch.float32)
+    k = torch.zeros((2, T, 64))
+    v = torch.zeros((2, T, 64))
+    k[:, :, 0] = ids
+    v[:, :, 3] = -ids
+    table = _table("affine")
+    cm_lib, cm_or = pst.CostModel(ROWS, LENS, table), oracle.CostTable(ROWS, LENS, table)
+    sess = DecodeSession(spec, k, v, page_size=P, max_new_tokens=max_new, extra_pages=64, host_only=True,
+                         plan_kw=dict(cost=cm_lib, num_bins=5, max_rows=16))
+    nodes = [[int(parent[i]), list(range(int(off[i]) + 1, int(off[i] + lens[i]) + 1)), True] for i in range(4)]
+    queries = [2, 3]
+    nxt = T + 1
+    rng = np.random.default_rng(5)
+    _session_model_check(sess, nodes, queries, P, cm_or)
+    appends = 0
+    for op in ["a", "b", "a", "a", "b", "p", "a", "b", "p", "a", "p", "b", "a", "a", "p", "b", "a"]:
+        B = len(queries)
+        if op == "a" and appends < max_new - 1:
+            kn = torch.zeros((B, 2, 64))
+            vn = torch.zeros((B, 2, 64))
+            for r, m in enumerate(queries):
+                kn[r, :, 0] = nxt
+                vn[r, :, 3] = -nxt
+                nodes[m][1].append(nxt)
+                nxt += 1
+            sess.append(kn, vn)
+            appends += 1
+            _session_model_check(sess, nodes, queries, P, cm_or, planned=False)
+            continue
+        elif op == "b":
+            qi, n = int(rng.integers(B)), int(rng.integers(1, 4))
+            kn = torch.zeros((n, 2, 64))
+            vn = torch.zeros((n, 2, 64))
+            new = []
+            for j in range(n):
+                kn[j, :, 0] = nxt
+                vn[j, :, 3] = -nxt
+                nodes.append([queries[qi], [nxt], True])
+                new.append(len(nodes) - 1)
+                nxt += 1
+            got = sess.branch(qi, kn, vn)
+            assert got == list(range(B, B + n - 1))
+            queries[qi] = new[0]
+            queries += new[1:]
+        elif op == "p" and B > 1:
+            qi = int(rng.integers(B))
+            del queries[qi]
+            live = set()
+            for m in queries:
+                while m >= 0:
+                    live.add(m)
+                    m = nodes[m][0]
+            for i, n in enumerate(nodes):
+                n[2] = n[2] and i in live
+            sess.prune(qi)
+        _session_model_check(sess, nodes, queries, P, cm_or)
+    with pytest.raises(ValueError):
+        sess.branch(0, torch.zeros((200, 2, 64)), torch.zeros((200, 2, 64)))  # more pages than the pool has
+    _session_model_check(sess, nodes, queries, P, cm_or, planned=False)  # a refused branch changes nothing
