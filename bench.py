@@ -47,6 +47,12 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="tree-shape sweep (2T..5T k-ary trees and a degenerate tree; CoDec's shapes): tree path, "
                          "tree path without splitting, and the query-guided baseline per shape")
+    ap.add_argument("--flatten-sweep", action="store_true",
+                    help="partition comparison (DEFT-Node, DEFT-Node-Chunk and DEFT-Flatten at several chunk "
+                         "lengths against the cost-model plan) on the large workloads and two tree shapes")
+    ap.add_argument("--flatten", type=int, default=0,
+                    help="> 0: time the DEFT-Flatten partition with chunks of this many tokens instead of the "
+                         "cost-model plan")
     ap.add_argument("--page-size", type=int, default=0,
                     help="> 0: K/V in a paged pool of pages of this many tokens (scattered, with holes)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "pac_traffic.json"),
@@ -192,6 +198,56 @@ def shape_sweep(torch, pst, workloads, a):
     }))
 
 
+def flatten_sweep(torch, pst, workloads, a):
+    """Partitions of the same tree (DEFT Table 6 and CoDec Fig. 10 analogs),
+    cold-cache PAC + POR each: one piece per node (DEFT-Node), nodes cut
+    into chunks of S_t tokens (DEFT-Node-Chunk), the depth-first flattening
+    cut into chunks of S_t tokens with bit causal masks (DEFT-Flatten), and
+    the cost-model plan."""
+    chunks = (128, 256, 512, 1024)
+    specs = [workloads.config("2"), workloads.config("3"), workloads.config("4"), workloads.config("5-mqa"),
+             workloads.kary_tree(2, 7), workloads.degenerate_tree(64)]
+    evict_bufs = (torch.empty(1 << 30, dtype=torch.uint8, device="cuda"),
+                  torch.empty(4096, dtype=torch.float32, device="cuda"))
+    rows = {}
+    for spec in specs:
+        print(f"[bench] partitions of {spec.name}", file=sys.stderr, flush=True)
+        q, k, v = workloads.make_tensors(spec, "cuda")
+        tree = pst.Tree.from_spec(spec, out_dtype="f32")
+        st = workload_stats(spec, tree)
+        out = torch.empty((spec.num_queries, spec.num_q_heads, spec.head_dim), device="cuda", dtype=torch.float32)
+        lse = torch.empty((spec.num_queries, spec.num_q_heads), device="cuda", dtype=torch.float32)
+        variants = [("cost_model", {}), ("node", {"no_split": True})]
+        variants += [(f"node_chunk_{c}", {"fixed_chunk": c}) for c in chunks]
+        variants += [(f"flatten_{c}", {"flatten": c}) for c in chunks]
+        r = {"queries": spec.num_queries, "nodes": spec.num_nodes, "unique_kv_bytes": st["unique_kv_bytes"]}
+        # An untimed pass first: the first variant timed after the inputs
+        # were made otherwise reads up to 10 % slow.
+        plan = pst.Plan(tree)
+        ws = pst.workspace(plan)
+        time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, 3, 3)
+        del ws, plan
+        for name, kw in variants:
+            plan = pst.Plan(tree, **kw)
+            ws = pst.workspace(plan)
+            pac, por, _ = time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, a.steps, a.warmup)
+            r[name + "_ms"] = statistics.mean(x + y for x, y in zip(pac, por))
+            r[name + "_tasks"] = int(len(plan.view()["tasks"]))
+            del ws, plan
+        best = min((c for c in chunks), key=lambda c: r[f"flatten_{c}_ms"])
+        r["flatten_best_chunk"] = best
+        r["cost_model_over_best_flatten"] = r[f"flatten_{best}_ms"] / r["cost_model_ms"]
+        r["unique_kv_frac_of_peak"] = st["unique_kv_bytes"] / (r["cost_model_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS
+        rows[spec.name] = r
+        del q, k, v, tree
+    print(json.dumps({
+        "metric": "partition comparison: PAC + POR ms per workload (DEFT-Node, -Node-Chunk, -Flatten, cost model)",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "higher_is_better": False, "dtype": "bf16",
+        "data": "synthetic", "config": {"mode": "flatten_sweep", "chunks": list(chunks)},
+        "workloads": rows,
+    }))
+
+
 def decode_loop_bench(torch, pst, workloads, spec, a):
     """Multi-step decoding: per step, append one token to every query's leaf
     and run PAC + POR; wall time per step includes the host length update
@@ -285,6 +341,9 @@ def main():
     if a.sweep:
         shape_sweep(torch, pst, workloads, a)
         return
+    if a.flatten_sweep:
+        flatten_sweep(torch, pst, workloads, a)
+        return
     spec = workloads.config(a.config)
     if a.decode_steps > 0:
         decode_loop_bench(torch, pst, workloads, spec, a)
@@ -300,7 +359,7 @@ def main():
     tree = pst.Tree.from_paged(spec, paged, out_dtype="f32") if paged else pst.Tree.from_spec(spec, out_dtype="f32")
     t_tree = (time.perf_counter() - t0) * 1e3
     t0 = time.perf_counter()
-    plan = pst.Plan(tree)
+    plan = pst.Plan(tree, flatten=a.flatten) if a.flatten else pst.Plan(tree)
     t_plan = (time.perf_counter() - t0) * 1e3
     st = workload_stats(spec, tree)
     pv = plan.view()
@@ -346,7 +405,8 @@ def main():
                    "head_dim": spec.head_dim, "nodes": spec.num_nodes, "queries": spec.num_queries,
                    "unique_kv_tokens": st["unique_kv_tokens"], "logical_tokens": st["logical_tokens"],
                    "cache": "cold (1 GiB read of an unrelated buffer before each step)", "plan_reused": True,
-                   "kv_layout": f"paged, {a.page_size}-token pages" if paged else "contiguous"},
+                   "kv_layout": f"paged, {a.page_size}-token pages" if paged else "contiguous",
+                   "partition": f"DEFT-Flatten, {a.flatten}-token chunks" if a.flatten else "cost model"},
         "unique_kv_GBps": st["unique_kv_bytes"] / (ms * 1e-3) / 1e9,
         "unique_kv_frac_of_peak": st["unique_kv_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "pac_ms": pac_avg,
@@ -364,7 +424,8 @@ def main():
     if os.path.exists(a.traffic):
         with open(a.traffic) as f:
             tr = json.load(f)
-        if tr.get("workload") == spec.name and tr.get("kernel_source_sha") == kernel_sha() and not paged:
+        if (tr.get("workload") == spec.name and tr.get("kernel_source_sha") == kernel_sha() and not paged
+                and not a.flatten):
             traffic = tr.get("hbm_bytes_per_launch")
     # Algorithmic work of one PAC launch: the unique KV bytes, and 4 d H_q
     # FLOPs per logical (query, token) (QK^T and PV).  The bound is the larger

@@ -152,7 +152,9 @@ pst_status pst_tree_build(const pst_tree_desc* desc, const pst_shape* shape, uin
 
 /* Decode-step growth: new lengths for every node, each >= the current one
  * (masked nodes stay <= 64).  Plans made from this tree stay valid: a node's
- * last piece simply grows.  Uploads the lengths on `stream`. */
+ * last piece simply grows.  Uploads the lengths on `stream`.
+ * PST_E_UNSUPPORTED (nothing changed) while a flattened plan of the tree
+ * is live. */
 pst_status pst_tree_set_lengths(pst_tree_t tree, const int32_t* kv_len, void* stream);
 
 /* Host views of the index, valid until the tree is freed. */
@@ -193,12 +195,15 @@ pst_status pst_cost_model_lookup(pst_cost_model_t cost, int32_t rows, int64_t le
 #define PST_PLAN_DOT_SMALL 8u    /* bf16 pieces of fewer than 16 rows take the wavefront dot-product path
                                     (the split CoDec and DEFT use); default: matrix cores for every bf16
                                     piece, which streams faster on gfx950 even at 1 row of 16 */
+#define PST_PLAN_FLATTEN 16u     /* DEFT-Flatten partition instead of the cost-model one (see below);
+                                    fixed_chunk = S_t, the chunk length (0 = 256) */
 typedef struct {
   int32_t num_bins;    /* workgroups per kv head; 0 = resident capacity / num_kv_heads */
   int32_t max_rows;    /* rows one workgroup holds (R_max); 0 = 256 (bf16) or 16 (f32); <= 256 */
   int32_t tile;        /* piece granularity G in tokens; 0 = 64; a multiple of 64 */
   int32_t grid_steps;  /* K of the grid search; 0 = 8 */
-  int32_t fixed_chunk; /* > 0: every node cut into pieces of this many tokens (ablation) */
+  int32_t fixed_chunk; /* > 0: every node cut into pieces of this many tokens (ablation);
+                          with PST_PLAN_FLATTEN: S_t, a multiple of 128 */
   uint32_t flags;
 } pst_plan_opts;
 
@@ -222,6 +227,29 @@ typedef struct {
 pst_status pst_plan(pst_tree_t tree, pst_cost_model_t cost, const pst_plan_opts* opts, void* stream,
                     pst_plan_t* out);
 
+/* PST_PLAN_FLATTEN (DEFT: Decoding with Flash Tree-Attention, section 3.3,
+ * remark 3.1, Fig. 3(c), and appendix A.9): the tree's K/V, in depth-first
+ * order, is one logical sequence cut into chunks of S_t tokens; a chunk may
+ * span nodes.  Each chunk is grouped with the queries that see any of its
+ * tokens, and a 64-bit bit causal mask per (query, 64 tokens of the chunk)
+ * says which ones.  K/V do not move: a per-token row table addresses them
+ * (either layout).
+ *  1. depth-first pre-order: roots, then children, by increasing node id;
+ *     nodes no query sees are left out;
+ *  2. chunk c = flattened tokens [c S_t, (c+1) S_t), the last one shorter;
+ *  3. a chunk's entries: the queries that see one of its tokens, ascending;
+ *  4. an entry's mask: S_t / 64 words, bit j of word w = token 64 w + j;
+ *  5. row groups of whole entries, at most min(R_max / g, 1024 / (S_t / 64))
+ *     entries: gq = ceil(entries / max) groups of ceil(entries / gq);
+ *  6. row groups onto num_bins workgroups by longest-processing-time list
+ *     scheduling on C_est(rows, chunk tokens), sorted by (cost desc, chunk,
+ *     group), each to the bin with the smallest (load, id);
+ *  7. a query's partial slots: one per chunk it is an entry of, in chunk order.
+ * Tasks then name the chunk in `node`, its first flattened token in
+ * `kv_begin`, and carry PST_TASK_FLAT.  Growth (pst_tree_set_lengths) is
+ * refused while a flattened plan of the tree is live: the flattening moves.
+ * PST_E_UNSUPPORTED when a kv head's K/V span more than 2^31 - 1 bytes. */
+
 /* Bytes of device workspace pst_decode_attn needs: the partial outputs
  * [num_slots][num_q_heads][head_dim] float32 plus their LSE
  * [num_slots][num_q_heads] float32, 256-byte aligned. */
@@ -230,17 +258,18 @@ pst_status pst_plan_workspace_size(pst_plan_t plan, size_t* bytes);
 /* Host views of a plan (bit-exact comparisons, introspection). */
 #define PST_TASK_FIELDS 8 /* node, piece, kv_begin, kv_len, row_begin, row_count, flags, reserved */
 #define PST_TASK_LAST_PIECE 1
+#define PST_TASK_FLAT 2 /* a flattened chunk (PST_PLAN_FLATTEN) */
 typedef struct {
   int32_t num_bins;
   int32_t num_tasks;
   int32_t num_queries;
   int32_t num_nodes;
   int64_t num_slots;
-  int64_t num_entries;
+  int64_t num_entries;           /* node->query entries; flattened plans: (chunk, query) entries */
   const int32_t* tasks;          /* [num_tasks][PST_TASK_FIELDS], bin-major, assignment order */
   const int32_t* bin_ptr;        /* [num_bins + 1] */
   const int64_t* slot_ptr;       /* [num_queries + 1] */
-  const int64_t* entry_slot;     /* [num_entries] first slot of each node->query entry */
+  const int64_t* entry_slot;     /* [num_entries] first slot of each entry */
   const int32_t* piece_len;      /* [num_nodes] Lp (0 for nodes no query passes) */
   const int32_t* b_eff;          /* [num_nodes] pieces per node */
   const int32_t* rows_per_group; /* [num_nodes] */
@@ -250,6 +279,12 @@ typedef struct {
   int32_t chosen_k;
   int32_t max_rows;
   int32_t mfma_min_rows;         /* bf16 pieces with at least this many rows use the matrix cores */
+  int32_t flat_chunk;            /* S_t of a flattened plan, else 0 (the arrays below are then NULL) */
+  int32_t num_chunks;
+  const int32_t* flat_ptr;       /* [num_chunks + 1] entries of each chunk */
+  const int32_t* flat_query;     /* [num_entries] query of each entry */
+  const uint64_t* flat_mask;     /* [num_entries][flat_chunk / 64] bit causal masks */
+  const int32_t* flat_rows;      /* [num_chunks * flat_chunk] pool row of each token, -1 past the end */
 } pst_plan_view;
 pst_status pst_plan_get(pst_plan_t plan, pst_plan_view* view);
 

@@ -21,6 +21,9 @@ Contents (each function cites the passage it follows):
   and the task partitioner, as read from CoDec's workload-balance section;
   the pages leave the exact procedure open, so these follow the library's
   stated reading step by step.
+* :mod:`oracle.flatten` -- DEFT's flattened tree KV splitting (depth-first
+  flattening, equal chunks, per-chunk query groups with 64-bit bit causal
+  masks), pinned against the attention oracle's visibility.
 
 Parity status: attention, merge and index are pinned by tests against
 brute force, closed forms, library routines and invariants.  The planner's
@@ -33,9 +36,10 @@ from .merge import por_pair, por_chain, flashdecoding_merge, lse_merge, streamin
 from .tree_index import build_index, TreeError
 from .cost import CostTable
 from .planner import plan
+from .flatten import flatten_plan
 
 __all__ = [
     "attend", "visible_tokens", "partial_attend",
     "por_pair", "por_chain", "flashdecoding_merge", "lse_merge", "streaming_merge",
-    "build_index", "TreeError", "CostTable", "plan",
+    "build_index", "TreeError", "CostTable", "plan", "flatten_plan",
 ]

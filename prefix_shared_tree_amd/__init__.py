@@ -44,7 +44,7 @@ _lib = C.CDLL(LIB_PATH)
 
 PST_F32, PST_BF16 = 0, 1
 TREE_HOST_ONLY = 1
-PLAN_QUERY_GUIDED, PLAN_NO_SPLIT, PLAN_HOST_ONLY, PLAN_DOT_SMALL = 1, 2, 4, 8
+PLAN_QUERY_GUIDED, PLAN_NO_SPLIT, PLAN_HOST_ONLY, PLAN_DOT_SMALL, PLAN_FLATTEN = 1, 2, 4, 8, 16
 TASK_FIELDS = 8
 
 STATUS = {
@@ -99,7 +99,9 @@ class _PlanView(C.Structure):
                 ("entry_slot", C.c_void_p), ("piece_len", C.c_void_p), ("b_eff", C.c_void_p),
                 ("rows_per_group", C.c_void_p), ("bin_load", C.c_void_p), ("makespan", C.c_int64),
                 ("cost_l", C.c_int64), ("chosen_k", C.c_int32), ("max_rows", C.c_int32),
-                ("mfma_min_rows", C.c_int32)]
+                ("mfma_min_rows", C.c_int32), ("flat_chunk", C.c_int32), ("num_chunks", C.c_int32),
+                ("flat_ptr", C.c_void_p), ("flat_query", C.c_void_p), ("flat_mask", C.c_void_p),
+                ("flat_rows", C.c_void_p)]
 
 
 _P = C.c_void_p
@@ -323,13 +325,18 @@ class Plan:
 
     def __init__(self, tree: Tree, cost: Optional[CostModel] = None, *, num_bins=0, max_rows=0, tile=0,
                  grid_steps=0, fixed_chunk=0, query_guided=False, no_split=False, host_only=False, stream=None,
-                 use_fitted=True, dot_small=False):
+                 use_fitted=True, dot_small=False, flatten=0):
+        """``flatten`` > 0: the DEFT-Flatten partition with chunks of that many
+        tokens (a multiple of 128) instead of the cost-model partition."""
         self.tree = tree
         if cost is None and use_fitted:
             cost = default_cost_model(tree.head_dim, tree.num_q_heads, tree.num_kv_heads, tree.in_dtype)
         self.cost = cost
         flags = (PLAN_QUERY_GUIDED if query_guided else 0) | (PLAN_NO_SPLIT if no_split else 0) | \
-                (PLAN_HOST_ONLY if host_only else 0) | (PLAN_DOT_SMALL if dot_small else 0)
+                (PLAN_HOST_ONLY if host_only else 0) | (PLAN_DOT_SMALL if dot_small else 0) | \
+                (PLAN_FLATTEN if flatten else 0)
+        if flatten:
+            fixed_chunk = int(flatten)
         opts = _PlanOpts(num_bins, max_rows, tile, grid_steps, fixed_chunk, flags)
         self._h = C.c_void_p()
         host = host_only or tree.host_only
@@ -353,6 +360,20 @@ class Plan:
             "b_eff": _view(v.b_eff, v.num_nodes, np.int32),
             "rows_per_group": _view(v.rows_per_group, v.num_nodes, np.int32),
             "bin_load": _view(v.bin_load, v.num_bins, np.int64),
+            **self._flat_view(v),
+        }
+
+    @staticmethod
+    def _flat_view(v) -> dict:
+        if not v.flat_chunk:
+            return {"flat_chunk": 0}
+        W = v.flat_chunk // 64
+        return {
+            "flat_chunk": v.flat_chunk, "num_chunks": v.num_chunks,
+            "flat_ptr": _view(v.flat_ptr, v.num_chunks + 1, np.int32),
+            "flat_query": _view(v.flat_query, v.num_entries, np.int32),
+            "flat_mask": _view(v.flat_mask, v.num_entries * W, np.uint64),
+            "flat_rows": _view(v.flat_rows, v.num_chunks * v.flat_chunk, np.int32),
         }
 
     def free(self):

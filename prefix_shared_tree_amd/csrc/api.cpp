@@ -124,6 +124,10 @@ struct pst_plan_s {
   int32_t* d_bin_ptr = nullptr;
   int32_t* d_entry_slot = nullptr;
   int64_t* d_slot_ptr = nullptr;
+  int32_t* d_flat_query = nullptr;  // flattened plans
+  uint64_t* d_flat_mask = nullptr;
+  int32_t* d_flat_rows = nullptr;
+  int64_t flat_pool_bytes = 0;      // bytes from a kv head's first row past the last row the plan reads
   std::vector<DevTask> dev_tasks;  // host copy of d_tasks
 };
 
@@ -150,6 +154,8 @@ static void free_plan_device(pst_plan_s* p) {
   p->d_tasks = nullptr;
   p->d_bin_ptr = p->d_entry_slot = nullptr;
   p->d_slot_ptr = nullptr;
+  p->d_flat_query = p->d_flat_rows = nullptr;
+  p->d_flat_mask = nullptr;
   p->on_device = false;
 }
 
@@ -278,6 +284,12 @@ pst_status pst_tree_set_lengths(pst_tree_t t, const int32_t* kv_len, void* strea
     return PST_E_INVALID_ARG;
   }
   TreeIndex& ix = t->ix;
+  for (const pst_plan_s* p : t->plans) {
+    if (p->r.flat_chunk > 0) {
+      set_error("a flattened plan of this tree is live: its chunks would move (free it, grow, plan again)");
+      return PST_E_UNSUPPORTED;
+    }
+  }
   for (int32_t i = 0; i < ix.N; ++i) {
     if (kv_len[i] < ix.kv_len[i]) {
       set_error("kv_len may only grow (node " + std::to_string(i) + ")");
@@ -454,6 +466,14 @@ pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* op
   po.no_split = (o.flags & PST_PLAN_NO_SPLIT) != 0;
   po.query_guided = (o.flags & PST_PLAN_QUERY_GUIDED) != 0;
   po.mfma_min_rows = (o.flags & PST_PLAN_DOT_SMALL) ? kMfmaMinRowsDot : 1;
+  if (o.flags & PST_PLAN_FLATTEN) {
+    if (po.no_split || po.query_guided || o.fixed_chunk < 0 || o.fixed_chunk % 128 != 0) {
+      set_error("PST_PLAN_FLATTEN takes no other partition flag and a chunk length that is a multiple of 128");
+      return PST_E_INVALID_ARG;
+    }
+    po.flat_chunk = o.fixed_chunk > 0 ? o.fixed_chunk : 256;
+    po.fixed_chunk = 0;
+  }
   const int32_t default_rows = t->shape.in_dtype == PST_F32 ? kMaxRowsDot : kMaxRows;
   po.r_max = o.max_rows > 0 ? o.max_rows : default_rows;
   if (po.tile % kTile != 0 || po.r_max > kMaxRows || po.fixed_chunk < 0 || po.fixed_chunk % kTile != 0 ||
@@ -495,7 +515,7 @@ pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* op
   p->tree = t;
   p->generation = t->generation;
   p->opts = po;
-  pst_status st = build_plan(t->ix, g, *cm, po, &p->r);
+  pst_status st = po.flat_chunk > 0 ? build_flat_plan(t->ix, g, *cm, po, &p->r) : build_plan(t->ix, g, *cm, po, &p->r);
   if (st != PST_OK) {
     delete p;
     return st;
@@ -505,6 +525,19 @@ pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* op
     set_error("too many partial slots");
     return PST_E_UNSUPPORTED;
   }
+  const bool flat = po.flat_chunk > 0;
+  if (flat) {
+    // Every row the plan reads must be addressable with 32-bit offsets from
+    // its kv head's first row.
+    int64_t max_row = -1;
+    for (int32_t r : p->r.flat_rows) max_row = std::max<int64_t>(max_row, r);
+    p->flat_pool_bytes = (max_row + 1) * t->shape.kv_stride_token * elem_bytes(t->shape.in_dtype);
+    if (p->flat_pool_bytes > INT32_MAX) {
+      delete p;
+      set_error("flattened plans address K/V with 32-bit offsets: a kv head spans more than 2^31 - 1 bytes");
+      return PST_E_UNSUPPORTED;
+    }
+  }
   if (!host_only) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::vector<int32_t> es32(p->r.entry_slot.begin(), p->r.entry_slot.end());
@@ -513,6 +546,35 @@ pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* op
     for (size_t i = 0; i < dt.size(); ++i) {
       const Task& a = p->r.tasks[i];
       DevTask& b = dt[i];
+      if (flat) {
+        // A chunk: its first entry of the row table and of the entry arrays.
+        // The mask test is needed unless every entry of the row group sees
+        // every token; a chunk over consecutive pool rows (inside one
+        // contiguous node, or nodes stored back to back) is addressed as a run.
+        b.tok0 = a.kv_begin;
+        b.node = a.node;
+        b.kv_begin = 0;
+        b.kv_len = a.kv_len;
+        b.e0 = p->r.flat_ptr[a.node];
+        b.row_begin = a.row_begin;
+        b.row_count = a.row_count;
+        b.piece = 0;
+        const int64_t W = p->r.flat_chunk / 64;
+        bool all_seen = true;
+        for (int64_t e = b.e0 + a.row_begin / g; all_seen && e < b.e0 + (a.row_begin + a.row_count) / g; ++e) {
+          for (int64_t w = 0; w < W && all_seen; ++w) {
+            const int64_t valid = std::min<int64_t>(64, std::max<int64_t>(0, a.kv_len - 64 * w));
+            const uint64_t need = valid == 64 ? ~0ull : ((1ull << valid) - 1);
+            all_seen = (p->r.flat_mask[e * W + w] & need) == need;
+          }
+        }
+        const int32_t* rows = p->r.flat_rows.data() + a.kv_begin;
+        bool linear = true;
+        for (int32_t k = 1; linear && k < a.kv_len; ++k) linear = rows[k] == rows[0] + k;
+        b.flags = (all_seen ? 0 : kDevMasked) | (linear ? kDevLinear : 0);
+        b.row0 = linear ? rows[0] : 0;
+        continue;
+      }
       // Contiguous: the piece's first pool token; paged: its position in the node.
       b.tok0 = t->ix.page_size > 0 ? a.kv_begin : t->ix.kv_offset[a.node] + a.kv_begin;
       b.node = a.node;
@@ -523,13 +585,18 @@ pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* op
       b.row_count = a.row_count;
       b.piece = a.piece;
       b.flags = ((a.flags & PST_TASK_LAST_PIECE) ? kDevLast : 0) | (t->ix.masked[a.node] ? kDevMasked : 0);
-      b.reserved = 0;
+      b.row0 = 0;
     }
     DevArena arena;
     arena.add(&p->d_tasks, dt.data(), dt.size());
     arena.add(&p->d_bin_ptr, p->r.bin_ptr.data(), p->r.bin_ptr.size());
     arena.add(&p->d_entry_slot, es32.data(), es32.size());
     arena.add(&p->d_slot_ptr, p->r.slot_ptr.data(), p->r.slot_ptr.size());
+    if (flat) {
+      arena.add(&p->d_flat_query, p->r.flat_query.data(), p->r.flat_query.size());
+      arena.add(&p->d_flat_mask, p->r.flat_mask.data(), p->r.flat_mask.size());
+      arena.add(&p->d_flat_rows, p->r.flat_rows.data(), p->r.flat_rows.size());
+    }
     st = arena.commit(&p->d_arena, s);
     if (st != PST_OK) {
       free_plan_device(p);
@@ -587,6 +654,13 @@ pst_status pst_plan_get(pst_plan_t p, pst_plan_view* v) {
   v->chosen_k = p->r.chosen_k;
   v->max_rows = p->opts.query_guided ? p->tree->shape.num_q_heads / p->tree->shape.num_kv_heads : p->opts.r_max;
   v->mfma_min_rows = p->tree->shape.in_dtype == PST_BF16 ? p->opts.mfma_min_rows : INT32_MAX;
+  const bool flat = p->r.flat_chunk > 0;
+  v->flat_chunk = p->r.flat_chunk;
+  v->num_chunks = flat ? static_cast<int32_t>(p->r.flat_ptr.size()) - 1 : 0;
+  v->flat_ptr = flat ? p->r.flat_ptr.data() : nullptr;
+  v->flat_query = flat ? p->r.flat_query.data() : nullptr;
+  v->flat_mask = flat ? p->r.flat_mask.data() : nullptr;
+  v->flat_rows = flat ? p->r.flat_rows.data() : nullptr;
   return PST_OK;
 }
 
@@ -642,6 +716,15 @@ pst_status pst_pac(pst_plan_t p, const void* q, const void* k, const void* v, vo
   pp.page_shift = t->ix.page_size > 0 ? __builtin_ctz(static_cast<unsigned>(t->ix.page_size)) : -1;
   pp.nq_mask = t->d_nq_mask;
   pp.entry_slot = p->d_entry_slot;
+  if (p->r.flat_chunk > 0) {
+    // Flattened chunks: entries, masks and rows of the plan; pages are in the row table.
+    pp.nq_idx = p->d_flat_query;
+    pp.nq_mask = p->d_flat_mask;
+    pp.flat_rows = p->d_flat_rows;
+    pp.mask_words = p->r.flat_chunk / 64;
+    pp.pool_bytes = p->flat_pool_bytes;
+    pp.page_shift = -1;
+  }
   pp.stride_head = t->shape.kv_stride_head;
   pp.stride_token = t->shape.kv_stride_token;
   pp.q_bytes = static_cast<int64_t>(t->ix.B) * t->shape.num_q_heads * t->shape.head_dim *

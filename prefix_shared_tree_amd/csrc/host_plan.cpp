@@ -295,4 +295,175 @@ pst_status build_plan(const TreeIndex& ix, int32_t g, const CostModel& cost, con
   return PST_OK;
 }
 
+
+// DEFT: Decoding with Flash Tree-Attention, section 3.3 (remark 3.1, Fig.
+// 3(c)) and appendix A.9: depth-first flattening of the tree KV, chunks of
+// S_t tokens, one group per chunk with every query that sees any of its
+// tokens and a 64-bit bit causal mask per (query, 64 tokens).  The reading
+// (traversal order, entry order, mask words, row groups, assignment, slots)
+// is the one stated with PST_PLAN_FLATTEN in pst.h, identical to the CPU
+// oracle's.
+pst_status build_flat_plan(const TreeIndex& ix, int32_t g, const CostModel& cost, const PlanOptions& o,
+                           PlanResult* out) {
+  const int32_t N = ix.N, B = ix.B, m = o.m;
+  const int64_t S = o.flat_chunk;
+  if (m < 1 || S <= 0 || S % 128 != 0) {
+    set_error("flattened plans need num_bins >= 1 and a chunk length that is a positive multiple of 128");
+    return PST_E_INVALID_ARG;
+  }
+  const int64_t W = S / 64;
+  const int64_t e_max = std::min<int64_t>(o.r_max / g, kMaskWordsMax / W);
+  if (e_max < 1) {
+    set_error("the chunk's masks or the GQA group do not fit one workgroup (lower the chunk length)");
+    return PST_E_UNSUPPORTED;
+  }
+  // 1. Depth-first pre-order over the nodes some query sees.
+  std::vector<std::vector<int32_t>> children(N);
+  std::vector<int32_t> stack, order;
+  for (int32_t i = N - 1; i >= 0; --i) {
+    if (ix.parent[i] < 0)
+      stack.push_back(i);
+    else
+      children[ix.parent[i]].push_back(i);
+  }
+  // Roots and children were collected from high id to low: pushed in that
+  // order, the lowest id is popped first.
+  while (!stack.empty()) {
+    const int32_t i = stack.back();
+    stack.pop_back();
+    if (ix.n_q[i] == 0) continue;
+    order.push_back(i);
+    for (int32_t c : children[i]) stack.push_back(c);
+  }
+  int64_t total = 0;
+  for (int32_t i : order) total += ix.kv_len[i];
+  const int64_t nchunks = cdiv(total, S);
+  if (nchunks * S > INT32_MAX) {
+    set_error("the flattened tree is too long");
+    return PST_E_UNSUPPORTED;
+  }
+  // 8. Pool row of every flattened token.
+  out->flat_chunk = static_cast<int32_t>(S);
+  out->flat_rows.assign(static_cast<size_t>(nchunks * S), -1);
+  {
+    int64_t t = 0;
+    for (int32_t i : order) {
+      for (int32_t j = 0; j < ix.kv_len[i]; ++j, ++t) {
+        int64_t row;
+        if (ix.page_size > 0)
+          row = static_cast<int64_t>(ix.page_idx[ix.page_ptr[i] + j / ix.page_size]) * ix.page_size + j % ix.page_size;
+        else
+          row = ix.kv_offset[i] + j;
+        if (row > INT32_MAX) {
+          set_error("a pool row beyond 2^31 - 1");
+          return PST_E_UNSUPPORTED;
+        }
+        out->flat_rows[t] = static_cast<int32_t>(row);
+      }
+    }
+  }
+  // 2-4. Chunks, their entries and masks, by node segments.
+  out->flat_ptr.assign(nchunks + 1, 0);
+  out->flat_query.clear();
+  out->flat_mask.clear();
+  std::vector<int64_t> chunk_len(nchunks, 0);
+  std::vector<uint64_t> words(static_cast<size_t>(B) * W, 0);
+  std::vector<uint8_t> seen(B, 0);
+  std::vector<int32_t> touched;
+  size_t seg = 0;      // index into order
+  int64_t seg_pos = 0;  // tokens of order[seg] already in earlier chunks
+  for (int64_t c = 0; c < nchunks; ++c) {
+    int64_t t0 = 0;  // chunk-relative position
+    const int64_t len = std::min<int64_t>(S, total - c * S);
+    chunk_len[c] = len;
+    while (t0 < len) {
+      const int32_t i = order[seg];
+      const int64_t take = std::min<int64_t>(ix.kv_len[i] - seg_pos, len - t0);
+      for (int32_t e = ix.nq_ptr[i]; e < ix.nq_ptr[i + 1]; ++e) {
+        const int32_t r = ix.nq_idx[e];
+        uint64_t* w = words.data() + static_cast<size_t>(r) * W;
+        bool any = false;
+        for (int64_t k = 0; k < take; ++k) {
+          const int64_t j = seg_pos + k;
+          if (ix.masked[i] && !((ix.nq_mask[e] >> j) & 1ull)) continue;
+          const int64_t tt = t0 + k;
+          w[tt >> 6] |= 1ull << (tt & 63);
+          any = true;
+        }
+        if (any && !seen[r]) {
+          seen[r] = 1;
+          touched.push_back(r);
+        }
+      }
+      t0 += take;
+      seg_pos += take;
+      if (seg_pos == ix.kv_len[i]) {
+        ++seg;
+        seg_pos = 0;
+      }
+    }
+    std::sort(touched.begin(), touched.end());
+    for (int32_t r : touched) {
+      out->flat_query.push_back(r);
+      uint64_t* w = words.data() + static_cast<size_t>(r) * W;
+      out->flat_mask.insert(out->flat_mask.end(), w, w + W);
+      std::fill(w, w + W, 0ull);
+      seen[r] = 0;
+    }
+    touched.clear();
+    out->flat_ptr[c + 1] = static_cast<int32_t>(out->flat_query.size());
+  }
+  // 5-6. Row groups of whole entries, placed by LPT.
+  std::vector<int64_t> epg(nchunks, 0);
+  std::vector<Item> items;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t ne = out->flat_ptr[c + 1] - out->flat_ptr[c];
+    if (ne == 0) continue;
+    const int64_t gq = cdiv(ne, e_max);
+    epg[c] = cdiv(ne, gq);
+    for (int64_t k = 0; k < gq; ++k) {
+      const int64_t n_ent = std::min<int64_t>(epg[c], ne - k * epg[c]);
+      items.push_back({cost.lookup(n_ent * g, chunk_len[c]), static_cast<int32_t>(c), static_cast<int32_t>(k), 0});
+    }
+  }
+  std::vector<std::vector<Item>> bins;
+  std::vector<int64_t> loads;
+  lpt(items, m, &bins, &loads);
+  out->bin_load = loads;
+  out->makespan = loads.empty() ? 0 : *std::max_element(loads.begin(), loads.end());
+  out->cost_l = 0;
+  out->chosen_k = 0;
+  out->piece_len.assign(N, 0);
+  out->b_eff.assign(N, 0);
+  out->rows_per_group.assign(N, 0);
+  out->tasks.clear();
+  out->bin_ptr.assign(m + 1, 0);
+  for (int32_t b = 0; b < m; ++b) {
+    for (const Item& it : bins[b]) {
+      const int64_t c = it.node;
+      const int64_t ne = out->flat_ptr[c + 1] - out->flat_ptr[c];
+      const int64_t n_ent = std::min<int64_t>(epg[c], ne - it.group * epg[c]);
+      Task t;
+      t.node = static_cast<int32_t>(c);
+      t.piece = 0;
+      t.kv_begin = static_cast<int32_t>(c * S);
+      t.kv_len = static_cast<int32_t>(chunk_len[c]);
+      t.row_begin = static_cast<int32_t>(it.group * epg[c] * g);
+      t.row_count = static_cast<int32_t>(n_ent * g);
+      t.flags = PST_TASK_FLAT;
+      t.reserved = 0;
+      out->tasks.push_back(t);
+    }
+    out->bin_ptr[b + 1] = static_cast<int32_t>(out->tasks.size());
+  }
+  // 7. One slot per (query, chunk), a query's in chunk order.
+  out->slot_ptr.assign(B + 1, 0);
+  for (int32_t r : out->flat_query) out->slot_ptr[r + 1]++;
+  for (int32_t r = 0; r < B; ++r) out->slot_ptr[r + 1] += out->slot_ptr[r];
+  std::vector<int64_t> cursor(out->slot_ptr.begin(), out->slot_ptr.end() - 1);
+  out->entry_slot.resize(out->flat_query.size());
+  for (size_t e = 0; e < out->flat_query.size(); ++e) out->entry_slot[e] = cursor[out->flat_query[e]]++;
+  return PST_OK;
+}
+
 }  // namespace pst

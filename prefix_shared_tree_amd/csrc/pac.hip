@@ -22,7 +22,12 @@
 // XOR-swizzled by 16-byte chunk so the reads below spread over the banks;
 // loads past the piece end return zeros.  Paged K/V (a node as a list of
 // pages of a paged pool) is a separate instantiation: each DMA block finds
-// its page through the page table (one scalar read per page run).
+// its page through the page table (one scalar read per page run).  So are
+// flattened chunks (DEFT: Decoding with Flash Tree-Attention, section 3.3
+// and appendix A.9: the depth-first tree KV cut into equal chunks that may
+// span nodes): each token's pool row comes from the plan's row table, and
+// every tile takes the test of the chunk's bit causal masks, which arrive
+// in LDS with the queries.
 //
 // Two compute paths, chosen per piece:
 //  * matrix cores (every bf16 piece by default): each wavefront owns 16 or 32
@@ -80,8 +85,17 @@ constexpr size_t kQOff = 2 * STAGE_BYTES + TILE_BYTES;
 constexpr size_t kAuxOff = kQOff + 64 * 1024;
 constexpr size_t kAuxBytes = 8 * 1024;  // softmax states exchanged between wavefronts; next task record
 constexpr size_t kLdsBytes = kAuxOff + kAuxBytes;
+// Flattened chunks add their bit causal masks (up to kMaskWordsMax words per
+// task) after the rest.
+constexpr size_t kMaskOff = kLdsBytes;
+constexpr size_t kMaskBytes = kMaskWordsMax * 8;
+constexpr size_t kLdsBytesFlat = kMaskOff + kMaskBytes;
 static_assert(kTileBytes >= 64 * 1024, "merge scratch reuses the tile stages");
-static_assert(kLdsBytes <= 160 * 1024, "one workgroup per compute unit");
+static_assert(kLdsBytesFlat <= 160 * 1024, "one workgroup per compute unit");
+
+// K/V layouts, one kernel instantiation each: contiguous node runs, paged
+// nodes, flattened chunks (every token addressed through the plan's row table).
+constexpr int kContig = 0, kPaged = 1, kFlat = 2;
 
 // The workgroup's LDS (dynamic size kLdsBytes), visible to every path as LDS.
 extern __shared__ __attribute__((aligned(16))) char pac_lds[];
@@ -195,6 +209,8 @@ struct Geo {
 
 struct TaskInfo {
   int piece, kv_begin, kv_len, row_begin, row_count, e0, masked, node;
+  int flat0;          // flattened chunk: its first token in the row table
+  int linear;         // flattened chunk over consecutive pool rows: addressed like a contiguous run
   const char* kbase;  // K of this kv head at the piece's first token (paged: at the pool's first row)
   const char* vbase;
 };
@@ -241,6 +257,46 @@ __device__ __forceinline__ void write_partial(const PacParams& p, const TaskInfo
   if (write_lse) p.lsepart[slot * p.hq + head] = lse;
 }
 
+// Flattened chunk: pool rows of N consecutive tokens from token `tok` of the
+// task (row table entries; wave-uniform, so scalar reads).
+template <int N>
+__device__ __forceinline__ void flat_rows_of(const PacParams& p, const TaskInfo& t, int tok, int* rw) {
+  const auto* fr = (const __attribute__((address_space(4))) int32_t*)(p.flat_rows) + t.flat0 + tok;
+#pragma unroll
+  for (int k = 0; k < N; ++k) rw[k] = fr[k];
+}
+// Buffer offset of lane `lane`'s chunk of 1 KB block b: token b TPB +
+// lane / CPT at pool row rw[lane / CPT] (an offset past the descriptor for
+// the -1 rows past the chunk's end, which then read zeros).
+template <int CPT, int TPB>
+__device__ __forceinline__ int flat_voff(const int* rw, int b, int lane, int64_t stb) {
+  const int P = b * 64 + lane;
+  const int tok = P / CPT, phys = P % CPT, j = lane / CPT;
+  int row = rw[0];
+#pragma unroll
+  for (int k = 1; k < TPB; ++k) row = j == k ? rw[k] : row;
+  const uint32_t off = static_cast<uint32_t>(static_cast<int64_t>(row) * stb) + ((phys ^ (tok & (CPT - 1))) << 4);
+  return static_cast<int>(row >= 0 ? off : 0x80000000u);
+}
+
+// Flattened chunk: the task's bit causal masks (mask_words words for each of
+// its entries, in entry order) into the mask area of LDS, one 1 KB DMA block
+// per wavefront at most.  Issued before the task's K/V, so the first tile's
+// wait covers it.
+template <int NW>
+__device__ __forceinline__ void issue_masks(const PacParams& p, const TaskInfo& t, int tid) {
+  static_assert(NW * 1024 >= kMaskBytes, "one block per wavefront holds the masks");
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int e_first = t.e0 + t.row_begin / p.g;
+  const int bytes = (t.row_count / p.g) * p.mask_words * 8;
+  const __amdgpu_buffer_rsrc_t r =
+      make_rsrc(reinterpret_cast<const char*>(p.nq_mask + static_cast<int64_t>(e_first) * p.mask_words), bytes);
+  if (w * 1024 < bytes) dma16(r, w * 1024 + lane * 16, lds_addr(pac_lds + kMaskOff + w * 1024));
+}
+__device__ __forceinline__ uint64_t flat_mask(const PacParams& p, int entry, int word) {
+  return reinterpret_cast<const uint64_t*>(pac_lds + kMaskOff)[entry * p.mask_words + word];
+}
+
 // DMA of tile `tile` of the piece into stage `stage`: the 16 1 KB blocks of
 // K and of V are spread over the NW wavefronts; lane L of a block fills
 // 16-byte chunk position P = block*64 + L, i.e. token P / CPT, chunk
@@ -256,6 +312,22 @@ __device__ __forceinline__ void issue_tile(const PacParams& p, const TaskInfo& t
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   char* st = pac_lds + stage * STAGE_BYTES;
   constexpr int KB = kHalfOps<NW>;
+  if (p.mask_words > 0 && !t.linear) {
+    // Flattened chunk: the rows of this wavefront's consecutive blocks come
+    // from the row table (scalar reads); K and V share them.
+    int rw[KB * TPB];
+    flat_rows_of<KB * TPB>(p, t, tok_base + KB * w * TPB, rw);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(t.kbase, p.pool_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(t.vbase, p.pool_bytes);
+#pragma unroll
+    for (int c = 0; c < KB; ++c) {
+      const int b = KB * w + c;
+      const int voff = flat_voff<G::CPT, TPB>(rw + c * TPB, b, lane, stb);
+      dma16(rk, voff, lds_addr(st + b * 1024));
+      dma16(rv, voff, lds_addr(st + TILE_BYTES + b * 1024));
+    }
+    return;
+  }
   if (p.page_shift >= 0 && (1 << p.page_shift) < G::TT) {
     // Pages shorter than a tile: consecutive blocks per wavefront, sharing
     // one page number when a page holds their tokens (see issue_half).
@@ -358,6 +430,20 @@ __device__ __forceinline__ void issue_half(const PacParams& p, const TaskInfo& t
   constexpr int TPB = 64 / G::CPT;  // tokens per 1 KB block
   const int tok_base = tile * G::TT;
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (p.mask_words > 0 && !t.linear) {
+    // Flattened chunk: this wavefront takes the consecutive blocks kHalfOps w
+    // .. kHalfOps w + kHalfOps - 1; their tokens' rows come from the row table.
+    constexpr int KB = kHalfOps<NW>;
+    int rw[KB * TPB];
+    flat_rows_of<KB * TPB>(p, t, tok_base + KB * w * TPB, rw);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, p.pool_bytes);
+#pragma unroll
+    for (int c = 0; c < KB; ++c) {
+      const int b = KB * w + c;
+      dma16(r, flat_voff<G::CPT, TPB>(rw + c * TPB, b, lane, stb), lds_addr(dst + b * 1024));
+    }
+    return;
+  }
   if (p.page_shift >= 0 && (1 << p.page_shift) < G::TT) {
     // Pages shorter than a tile: this wavefront takes the consecutive blocks
     // kHalfOps w .. kHalfOps w + kHalfOps - 1, which share one page when a
@@ -472,7 +558,14 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     slot0[rb] = p.entry_slot[entry];
     qhead[rb] = head;
     rmask[rb] = ~0ull;
-    if (t.masked && qok[rb]) rmask[rb] = p.nq_mask[entry];
+    if (p.mask_words == 0 && t.masked && qok[rb]) rmask[rb] = p.nq_mask[entry];
+  }
+  // Flattened chunk: each row's entry among the task's (row groups hold
+  // whole entries), which indexes its masks in LDS.
+  int mrow[RBR] = {};
+  if (p.mask_words > 0) {
+#pragma unroll
+    for (int rb = 0; rb < RBR; ++rb) mrow[rb] = qok[rb] ? (slab * ROWS_W + rb * 16 + l16) / p.g : 0;
   }
 
   // Queries first (needed first), then groups 0..2.
@@ -482,6 +575,7 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     for (int o = 0; o < QOPS; ++o)
       if (o * NW + w < qops_total) dma16(rq, static_cast<int>(qoff[o]), lds_addr(qarea + (o * NW + w) * 1024));
   }
+  if (p.mask_words > 0) issue_masks<NW>(p, t, tid);
   if (0 < nt) issue_half<D, NW>(p, t, t.kbase, stb, 0, kslot(0), tid);
   if (1 < nt) issue_half<D, NW>(p, t, t.kbase, stb, 1, kslot(1), tid);
   if (0 < nt) issue_half<D, NW>(p, t, t.vbase, stb, 0, vslot(0), tid);
@@ -595,15 +689,31 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[rb][j] = s[j >> 2][rb][j & 3];
     if constexpr (kVis) {
+      if (p.mask_words > 0) {
+        // Flattened chunk: the 32 tokens of this step lie in one 64-token
+        // mask word (tiles are multiples of 64 tokens); clear bits past the
+        // chunk's end.
+        const int word = (tile * G::TT + ts) >> 6;
 #pragma unroll
-      for (int rb = 0; rb < RBR; ++rb)
+        for (int rb = 0; rb < RBR; ++rb) {
+          const uint64_t mk = flat_mask(p, mrow[rb], word);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int tt = tile * G::TT + ts + (j >> 2) * 16 + lg * 4 + (j & 3);
-          const int bit = t.kv_begin + tt;
-          const bool vis = tt < t.kv_len && (bit >= 64 || ((rmask[rb] >> bit) & 1ull));
-          x[rb][j] = vis ? x[rb][j] : kNegInf;
+          for (int j = 0; j < 8; ++j) {
+            const int bit = (ts + (j >> 2) * 16 + lg * 4 + (j & 3)) & 63;
+            x[rb][j] = ((mk >> bit) & 1ull) ? x[rb][j] : kNegInf;
+          }
         }
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < RBR; ++rb)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int tt = tile * G::TT + ts + (j >> 2) * 16 + lg * 4 + (j & 3);
+            const int bit = t.kv_begin + tt;
+            const bool vis = tt < t.kv_len && (bit >= 64 || ((rmask[rb] >> bit) & 1ull));
+            x[rb][j] = vis ? x[rb][j] : kNegInf;
+          }
+      }
     }
     // Reference maximum m (scaled units) per row, raised only when the row's
     // maximum exceeds it by more than kLazy (then p <= 2^kLazy, harmless in
@@ -935,6 +1045,7 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
   const int R = t.row_count;
   const int r0 = rs * RL;
 
+  if (p.mask_words > 0) issue_masks<NW>(p, t, tid);
   issue_prologue<D, EB, NW>(p, t, stb, tid);
 
   // Branch-free gather (dead rows read row 0 of the task and are zeroed).
@@ -982,6 +1093,8 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
   // Visibility of token tt of the piece for row r of this lane.
   auto visible = [&](int r, int tt) {
     if (tt >= t.kv_len) return false;
+    if (p.mask_words > 0)  // flattened chunk (row groups hold whole entries)
+      return ((flat_mask(p, (r0 + r) / p.g, tt >> 6) >> (tt & 63)) & 1ull) != 0;
     if (!t.masked) return true;
     const int bit = t.kv_begin + tt;
     if (bit >= 64) return true;
@@ -1114,14 +1227,18 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
   }
 }
 
-// PAGED selects the instantiation for the paged K/V layout; the contiguous
-// one is compiled without the page-table code (its registers and scalar
-// registers stay with the tile loop).
-template <typename T, int D, bool PAGED>
+// LAYOUT selects the instantiation (kContig, kPaged, kFlat); each is
+// compiled without the other layouts' addressing code (its registers and
+// scalar registers stay with the tile loop).
+template <typename T, int D, int LAYOUT>
 __global__ __launch_bounds__(kWaves<T> * 64) __attribute__((amdgpu_waves_per_eu(kWaves<T> / 4, kWaves<T> / 4)))
 void pac_kernel(PacParams p) {
   constexpr int NW = kWaves<T>;
-  if constexpr (!PAGED) p.page_shift = -1;  // every page-table branch folds away
+  if constexpr (LAYOUT != kPaged) p.page_shift = -1;  // every page-table branch folds away
+  if constexpr (LAYOUT != kFlat)
+    p.mask_words = 0;  // and every row-table branch
+  else
+    __builtin_assume(p.mask_words > 0);
   const int bin = blockIdx.x % p.num_bins;
   const int kvh = blockIdx.x / p.num_bins;
   const int tb = p.bin_ptr[bin], te = p.bin_ptr[bin + 1];
@@ -1152,9 +1269,17 @@ void pac_kernel(PacParams p) {
     const int64_t tok0 = (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(task.tok0 >> 32))) << 32) |
                          static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(task.tok0)));
     t.node = __builtin_amdgcn_readfirstlane(task.node);
-    // Contiguous: K/V at the piece's first token; paged: the head's pool
-    // start (blocks add their page rows).
-    const int64_t off = (kvh * p.stride_head + (p.page_shift >= 0 ? 0 : tok0) * p.stride_token) * esz;
+    t.flat0 = static_cast<int>(tok0);
+    t.linear = (__builtin_amdgcn_readfirstlane(task.flags) & kDevLinear) != 0;
+    // Contiguous: K/V at the piece's first token; paged and flattened: the
+    // head's pool start (blocks add their rows), or for a flattened chunk
+    // over consecutive rows its first row.
+    int64_t first = p.page_shift >= 0 ? 0 : tok0;
+    if (p.mask_words > 0)
+      first = t.linear ? (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(task.row0 >> 32))) << 32) |
+                             static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(task.row0)))
+                       : 0;
+    const int64_t off = (kvh * p.stride_head + first * p.stride_token) * esz;
     t.kbase = static_cast<const char*>(p.k) + off;
     t.vbase = static_cast<const char*>(p.v) + off;
     bool done = false;
@@ -1178,23 +1303,25 @@ void pac_kernel(PacParams p) {
   }
 }
 
-template <typename T, int D, bool PAGED>
+template <typename T, int D, int LAYOUT>
 int launch_layout(const PacParams& p, void* stream) {
   const int grid = p.num_bins * p.hkv;
+  constexpr size_t lds = LAYOUT == kFlat ? kLdsBytesFlat : kLdsBytes;
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pac_kernel<T, D, PAGED>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pac_kernel<T, D, LAYOUT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return static_cast<int>(e);
     configured = true;
   }
-  hipLaunchKernelGGL((pac_kernel<T, D, PAGED>), dim3(grid), dim3(kWaves<T> * 64), kLdsBytes,
+  hipLaunchKernelGGL((pac_kernel<T, D, LAYOUT>), dim3(grid), dim3(kWaves<T> * 64), lds,
                      static_cast<hipStream_t>(stream), p);
   return static_cast<int>(hipGetLastError());
 }
 template <typename T, int D>
 int launch_one(const PacParams& p, void* stream) {
-  return p.page_shift >= 0 ? launch_layout<T, D, true>(p, stream) : launch_layout<T, D, false>(p, stream);
+  if (p.mask_words > 0) return launch_layout<T, D, kFlat>(p, stream);
+  return p.page_shift >= 0 ? launch_layout<T, D, kPaged>(p, stream) : launch_layout<T, D, kContig>(p, stream);
 }
 
 }  // namespace
@@ -1210,13 +1337,13 @@ int launch_pac(const PacParams& p, int in_dtype, int head_dim, void* stream) {
 int pac_blocks_per_cu(int in_dtype, int head_dim, int* blocks) {
   hipError_t e;
   if (in_dtype == PST_BF16 && head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 128, false>, kWaves<uint16_t> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 128, kContig>, kWaves<uint16_t> * 64, kLdsBytes);
   else if (in_dtype == PST_BF16)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 64, false>, kWaves<uint16_t> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 64, kContig>, kWaves<uint16_t> * 64, kLdsBytes);
   else if (head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 128, false>, kWaves<float> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 128, kContig>, kWaves<float> * 64, kLdsBytes);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 64, false>, kWaves<float> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 64, kContig>, kWaves<float> * 64, kLdsBytes);
   return static_cast<int>(e);
 }
 

@@ -45,12 +45,14 @@ struct DevTask {
   int32_t row_begin;
   int32_t row_count;
   int32_t piece;
-  int32_t flags;    // kDevLast | kDevMasked
-  int64_t reserved;
+  int32_t flags;    // kDevLast | kDevMasked | kDevLinear
+  int64_t row0;     // kDevLinear: pool row of the chunk's first token (its rows are consecutive)
 };
 static_assert(sizeof(DevTask) == 48, "device task layout");
 constexpr int32_t kDevLast = 1;
-constexpr int32_t kDevMasked = 2;
+constexpr int32_t kDevMasked = 2;  // the task needs the mask test (a masked node, a chunk whose masks are not all ones)
+constexpr int32_t kDevLinear = 4;  // flattened chunk over consecutive pool rows (addressed as a contiguous run)
+constexpr int32_t kMaskWordsMax = 1024;  // mask words of one flattened task (8 KB of LDS)
 
 struct CostModel {
   uint32_t magic = kCostMagic;
@@ -85,6 +87,7 @@ struct PlanOptions {
   bool no_split = false;
   bool query_guided = false;
   int32_t mfma_min_rows = 1;
+  int32_t flat_chunk = 0;  // > 0: flattened partition with chunks of this many tokens
 };
 
 struct PlanResult {
@@ -95,9 +98,16 @@ struct PlanResult {
   std::vector<int64_t> bin_load;
   int64_t makespan = 0, cost_l = 0;
   int32_t chosen_k = 0;
+  // Flattened partition (flat_chunk > 0): entries are (chunk, query) pairs;
+  // entry_slot holds each entry's slot.
+  int32_t flat_chunk = 0;
+  std::vector<int32_t> flat_ptr, flat_query, flat_rows;
+  std::vector<uint64_t> flat_mask;
 };
 pst_status build_plan(const TreeIndex& ix, int32_t g, const CostModel& cost, const PlanOptions& o,
                       PlanResult* out);
+pst_status build_flat_plan(const TreeIndex& ix, int32_t g, const CostModel& cost, const PlanOptions& o,
+                           PlanResult* out);
 CostModel analytic_cost_model(int32_t g, int32_t head_dim, int32_t elem_bytes);
 
 // ---------------------------------------------------------------------------
@@ -126,6 +136,9 @@ struct PacParams {
   int32_t g;
   int32_t mfma_min_rows;  // bf16 pieces with at least this many rows use the matrix cores
   float scale_log2;       // scale * log2(e)
+  int32_t mask_words;       // flattened plans: 64-bit mask words per entry (S_t / 64); 0 otherwise
+  const int32_t* flat_rows; // flattened plans: pool row of every chunk token (-1 past a chunk's end); tok0 indexes it
+  int64_t pool_bytes;       // flattened plans: bytes from a kv head's first row past the last row read
 };
 
 struct PorParams {

@@ -205,6 +205,63 @@ def test_paged_config_sampled(name, P):
     check(spec, (q, k, v), out, lse, queries=sample(spec.num_queries, 16, 11))
 
 
+FLAT_CASES = [
+    # seed, dtype, H_kv, g, d, chunk, page (0 = contiguous), masked fraction, max queries, dot_small
+    (0, "bf16", 2, 4, 128, 128, 0, 0.0, 40, False),
+    (1, "bf16", 1, 32, 128, 256, 0, 0.0, 12, False),   # many rows: the one-slab-per-wave layout
+    (2, "bf16", 2, 4, 64, 256, 0, 0.4, 40, False),     # head dim 64 (128-token tiles, two mask words), masked nodes
+    (3, "f32", 2, 4, 64, 128, 0, 0.0, 12, False),      # float32 dot path
+    (4, "f32", 1, 4, 128, 384, 0, 0.4, 12, False),     # float32, 32-token tiles
+    (5, "bf16", 4, 1, 128, 512, 0, 0.4, 40, True),     # bf16 dot path below 16 rows
+    (6, "bf16", 2, 8, 128, 1024, 0, 0.0, 40, False),   # 16 mask words: few entries per row group
+    (7, "bf16", 2, 4, 128, 256, 16, 0.4, 40, False),   # paged pool (NaN in page tails and holes)
+    (8, "f32", 2, 4, 128, 128, 8, 0.0, 12, False),     # paged, float32
+]
+
+
+@pytest.mark.parametrize("case", FLAT_CASES, ids=[f"flat{c[0]}" for c in FLAT_CASES])
+def test_flatten_parity(case):
+    """DEFT-Flatten partition: chunks span nodes, every tile takes the bit
+    causal mask test, K/V rows come from the row table."""
+    seed, dtype, hkv, g, d, chunk, P, masked, maxq, dot_small = case
+    spec = workloads.random_tree(3000 + seed, max_nodes=10, max_len=700, max_queries=maxq, num_q_heads=hkv * g,
+                                 num_kv_heads=hkv, head_dim=d, dtype=dtype, masked_prob=masked)
+    say(f"flat case {seed}: chunk {chunk} page {P} dtype {dtype} H {hkv * g}/{hkv} d {d} "
+        f"N {spec.num_nodes} B {spec.num_queries}")
+    q, k, v = workloads.make_tensors(spec, "cuda")
+    if P:
+        paged, kp, vp = workloads.page_pools(spec, k, v, P, spare_pages=1)
+        tree = pst.Tree.from_paged(spec, paged, out_dtype="f32")
+    else:
+        kp, vp = k, v
+        tree = pst.Tree.from_spec(spec, out_dtype="f32")
+    plan = pst.Plan(tree, num_bins=6, flatten=chunk, dot_small=dot_small,
+                    max_rows=16 if dtype == "f32" else 0)
+    out, lse = pst.decode_attn(plan, q, kp, vp)
+    torch.cuda.synchronize()
+    check(spec, (q, k, v), out, lse)
+
+
+@pytest.mark.parametrize("name,chunk", [("1", 256), ("3", 512), ("4", 256), ("2", 1024), ("5-mqa", 256)])
+def test_flatten_config(name, chunk):
+    """Whole workloads under the flattened partition, checked against the
+    oracle (sampled queries on the large ones) and against the cost-model
+    plan's output."""
+    spec = workloads.config(name)
+    q, k, v = workloads.make_tensors(spec, "cuda")
+    tree = pst.Tree.from_spec(spec, out_dtype="f32")
+    flat = pst.Plan(tree, flatten=chunk)
+    say(f"config {name} flattened by {chunk}: {flat.view()['num_chunks']} chunks, {len(flat.view()['tasks'])} tasks")
+    out, lse = pst.decode_attn(flat, q, k, v)
+    ref, rlse = pst.decode_attn(pst.Plan(tree), q, k, v)
+    torch.cuda.synchronize()
+    queries = list(range(spec.num_queries)) if spec.num_queries <= 16 else sample(spec.num_queries, 16, 5)
+    check(spec, (q, k, v), out, lse, queries=queries)
+    tol = TOL[spec.dtype]
+    assert (out - ref).abs().max().item() <= 2 * tol
+    assert (lse - rlse).abs().max().item() <= 8 * max(tol, 1e-5)
+
+
 def test_max_rows_split():
     """More rows than one workgroup holds: the planner cuts row groups (> 256 rows)."""
     lens = [700] + [3] * 20

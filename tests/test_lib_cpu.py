@@ -383,3 +383,75 @@ def test_decode_session_branch_prune_bookkeeping():
     with pytest.raises(ValueError):
         sess.branch(0, torch.zeros((200, 2, 64)), torch.zeros((200, 2, 64)))  # more pages than the pool has
     _session_model_check(sess, nodes, queries, P, cm_or, planned=False)  # a refused branch changes nothing
+
+
+FLAT_CASES = [(128, 256, 5), (256, 16, 3), (512, 256, 32), (1024, 8, 7), (640, 64, 1)]
+
+
+@pytest.mark.parametrize("chunk,r_max,m", FLAT_CASES)
+@pytest.mark.parametrize("spec", _specs()[::2] + [workloads.config("4")], ids=lambda s: s.name)
+def test_flatten_plan_bit_exact(spec, chunk, r_max, m):
+    """DEFT-Flatten partition: the library's tasks, bins, entries, masks, row
+    table and slots equal the oracle's."""
+    from oracle.flatten import flatten_plan
+
+    if spec.dtype == "f32":
+        r_max = min(r_max, 16)
+    if spec.group > r_max:
+        pytest.skip("GQA group larger than a row group")
+    table = _table("random", seed=chunk)
+    cm = pst.CostModel(ROWS, LENS, table)
+    plan = pst.Plan(_tree(spec), cm, num_bins=m, max_rows=r_max, flatten=chunk, host_only=True)
+    got = plan.view()
+    ix = oracle.build_index(spec)
+    want = flatten_plan(ix, spec.parent, spec.kv_len, spec.node_masked, spec.group,
+                        oracle.CostTable(ROWS, LENS, table), m, chunk=chunk, r_max=r_max, kv_offset=spec.kv_offset)
+    assert got["flat_chunk"] == chunk
+    assert np.array_equal(got["tasks"][:, :7], want["tasks"])
+    for key in ("bin_ptr", "slot_ptr", "bin_load", "flat_ptr", "flat_query", "flat_mask", "flat_rows"):
+        assert np.array_equal(got[key], want[key].astype(got[key].dtype)), key
+    assert np.array_equal(got["entry_slot"], want["flat_slot"])
+    assert got["makespan"] == want["makespan"] and got["num_slots"] == want["num_slots"]
+
+
+@pytest.mark.parametrize("page", [8, 32])
+def test_flatten_plan_paged_bit_exact(page):
+    from oracle.flatten import flatten_plan
+
+    spec = workloads.config("3")
+    paged = _paged_tables(spec, page)
+    tree = pst.Tree.from_paged(spec, paged, host_only=True)
+    table = _table("affine")
+    plan = pst.Plan(tree, pst.CostModel(ROWS, LENS, table), num_bins=16, flatten=256, host_only=True)
+    got = plan.view()
+    ix = oracle.build_index(spec)
+    want = flatten_plan(ix, spec.parent, spec.kv_len, None, spec.group, oracle.CostTable(ROWS, LENS, table), 16,
+                        chunk=256, page_size=page, page_ptr=paged["page_ptr"], page_idx=paged["page_idx"])
+    for key in ("flat_rows", "flat_mask", "flat_query"):
+        assert np.array_equal(got[key], want[key].astype(got[key].dtype)), key
+    assert np.array_equal(got["tasks"][:, :7], want["tasks"])
+
+
+def _paged_tables(spec, page):
+    """Page tables with scattered page numbers (no K/V needed on the host)."""
+    rng = np.random.default_rng(page)
+    npg = (np.asarray(spec.kv_len, dtype=np.int64) + page - 1) // page
+    page_ptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    page_idx = rng.permutation(int(page_ptr[-1]) + 7)[:int(page_ptr[-1])].astype(np.int32)
+    return {"page_size": page, "page_ptr": page_ptr, "page_idx": page_idx}
+
+
+def test_flatten_options_and_growth():
+    spec = workloads.config("1")
+    t = _tree(spec)
+    _raises("PST_E_INVALID_ARG", pst.Plan, t, num_bins=4, flatten=192, host_only=True)  # not a multiple of 128
+    _raises("PST_E_INVALID_ARG", pst.Plan, t, num_bins=4, flatten=256, no_split=True, host_only=True)
+    _raises("PST_E_INVALID_ARG", pst.Plan, t, num_bins=4, flatten=256, query_guided=True, host_only=True)
+    p = pst.Plan(t, num_bins=4, flatten=256, host_only=True)
+    before = t.index()["visible"].copy()
+    longer = spec.kv_len.copy()
+    _raises("PST_E_UNSUPPORTED", t.set_lengths, longer)  # refused while a flattened plan is live
+    assert np.array_equal(t.index()["visible"], before)
+    p.free()
+    t.set_lengths(longer)  # allowed again
+    t.free()
