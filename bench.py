@@ -269,8 +269,10 @@ def decode_loop_bench(torch, pst, workloads, spec, a):
     out = torch.empty((B, hq, d), device="cuda", dtype=torch.float32)
     lse = torch.empty((B, hq), device="cuda", dtype=torch.float32)
     results = {}
-    for name, every in (("reuse", 0), ("replan_every_16", 16), ("replan_every_step", 1)):
-        sess = DecodeSession(spec, k, v, page_size=P, max_new_tokens=S, replan_every=every)
+    policies = (("reuse", 0, {}), ("replan_every_16", 16, {}), ("replan_every_step", 1, {}),
+                ("flatten_256_replan_every_step", 0, {"flatten": 256}))
+    for name, every, kw in policies:
+        sess = DecodeSession(spec, k, v, page_size=P, max_new_tokens=S, replan_every=every, plan_kw=kw)
         torch.cuda.synchronize()
         gpu = []
         t0 = time.perf_counter()

@@ -13,7 +13,9 @@ extends, with spare pages reserved for growth.
 * ``append``: one token per query into its leaf's next slot; the lengths
   change in place (``pst_tree_set_lengths``: the last piece of every grown
   node absorbs the growth, so the plan stays valid); re-plan on a fixed
-  period (``replan_every`` steps; 0 = never).
+  period (``replan_every`` steps; 0 = never).  With a flattened partition
+  (``plan_kw={"flatten": S_t}``) every step plans again: growth moves the
+  chunks.
 * ``branch``: a query's leaf becomes an inner node and gets new one-token
   leaves, one for the query and one for each new query that forks from it.
 * ``prune``: a query finishes; the nodes only it used go back to the free
@@ -122,7 +124,8 @@ class DecodeSession:
 
     def _replan(self):
         t0 = time.perf_counter()
-        self.plan.free()
+        if self.plan is not None:
+            self.plan.free()
         self._make_plan()
         self.replan_s += time.perf_counter() - t0
         self.replans += 1
@@ -163,9 +166,17 @@ class DecodeSession:
         self.k[:, rows] = k_new.transpose(0, 1).to(self.k.dtype)
         self.v[:, rows] = v_new.transpose(0, 1).to(self.v.dtype)
         self.kv_len[qn] += 1
-        self.tree.set_lengths(self.kv_len)
         self.steps += 1
         self.steps_since_plan += 1
+        if self.plan_kw.get("flatten"):
+            # A flattened partition's chunks move when a node grows: plan again
+            # every step (the tree refuses growth while such a plan is live).
+            self.plan.free()
+            self.plan = None
+            self.tree.set_lengths(self.kv_len)
+            self._replan()
+            return
+        self.tree.set_lengths(self.kv_len)
         if self.replan_every and self.steps_since_plan >= self.replan_every:
             self._replan()
 

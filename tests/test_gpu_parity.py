@@ -404,6 +404,42 @@ def test_decode_session_steps(replan_every):
 
 
 @pytest.mark.gpu
+def test_decode_session_flatten():
+    """A decode session under the DEFT-Flatten partition: appends re-plan
+    every step, forks and finishes rebuild; each step against the oracle."""
+    from prefix_shared_tree_amd.decode_loop import DecodeSession
+
+    parent = np.array([-1, 0, 0, 1])
+    lens = np.array([300, 90, 7, 64])
+    off = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    spec0 = workloads.TreeSpec("flatdecode", parent, lens, off, np.array([2, 3]), 16, 4, 128, "bf16", 23)
+    q, k, v = workloads.make_tensors(spec0, "cuda")
+    sess = DecodeSession(spec0, k, v, page_size=16, max_new_tokens=6, extra_pages=40,
+                         plan_kw=dict(num_bins=4, flatten=128))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+
+    def rows(n):
+        return torch.randn((n, 4, 128), generator=g, device="cuda").to(torch.bfloat16)
+
+    for op in ["a", "b2", "a", "a", "p0", "a"]:
+        if op == "a":
+            sess.append(rows(sess.num_queries), rows(sess.num_queries))
+        elif op[0] == "b":
+            sess.branch(0, rows(int(op[1])), rows(int(op[1])))
+        else:
+            sess.prune(int(op[1]))
+        parent, kv_len, koff, qn, kc, vc = sess.contiguous()
+        spec = workloads.TreeSpec("flatdecode", parent, kv_len, koff, qn, 16, 4, 128, "bf16", 23)
+        qs = torch.randn((sess.num_queries, 16, 128), generator=g, device="cuda").to(torch.bfloat16)
+        out, lse = sess.decode(qs)
+        torch.cuda.synchronize()
+        assert sess.plan.view()["flat_chunk"] == 128
+        say(f"{op}: {sess.num_queries} queries, {len(kv_len)} nodes, replans {sess.replans}")
+        check(spec, (qs, kc, vc), out, lse)
+
+
+@pytest.mark.gpu
 def test_decode_session_branch_prune():
     """Tree search over a paged pool: queries grow, fork and finish; after every
     change each query's attention is checked against the oracle on the tree the
