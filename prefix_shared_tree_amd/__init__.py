@@ -148,8 +148,9 @@ def _view(ptr, count, dtype):
 
 
 def _stream(stream):
+    """A hipStream_t for the C ABI: a raw handle, a torch stream, or None (torch's current stream)."""
     if stream is not None:
-        return C.c_void_p(int(stream))
+        return C.c_void_p(int(getattr(stream, "cuda_stream", stream)))
     import torch
 
     if torch.cuda.is_available():

@@ -262,6 +262,40 @@ def test_flatten_config(name, chunk):
     assert (lse - rlse).abs().max().item() <= 8 * max(tol, 1e-5)
 
 
+def test_graph_capture_replays():
+    """PAC + POR captured in a graph (several layers' worth, as a decode step
+    would be): the calls allocate nothing and set no memory, so every replay,
+    with eager work and synchronisation between them, equals the eager
+    result bit for bit."""
+    spec = workloads.config("3")
+    q, k, v = workloads.make_tensors(spec, "cuda")
+    tree = pst.Tree.from_spec(spec, out_dtype="f32")
+    plan = pst.Plan(tree)
+    ws = pst.workspace(plan)
+    out = torch.empty((spec.num_queries, spec.num_q_heads, spec.head_dim), device="cuda")
+    lse = torch.empty((spec.num_queries, spec.num_q_heads), device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        pst.decode_attn(plan, q, k, v, out=out, lse=lse, ws=ws)
+    s.synchronize()
+    ref, rlse = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(4):
+            pst.pac(plan, q, k, v, ws, stream=s)
+            pst.por(plan, out, lse, ws, stream=s)
+    for rep in range(5):
+        out.fill_(float("nan"))
+        lse.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        s.synchronize()
+        say(f"  replay {rep}: max|dO| {(out - ref).abs().max().item():.1e}")
+        assert torch.equal(out, ref) and torch.equal(lse, rlse)
+    check(spec, (q, k, v), out, lse, queries=sample(spec.num_queries, 8, 3))
+
+
 def test_max_rows_split():
     """More rows than one workgroup holds: the planner cuts row groups (> 256 rows)."""
     lens = [700] + [3] * 20
