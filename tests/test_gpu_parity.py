@@ -296,6 +296,40 @@ def test_graph_capture_replays():
     check(spec, (q, k, v), out, lse, queries=sample(spec.num_queries, 8, 3))
 
 
+def test_injected_allocation_failure():
+    """A device allocation forced to fail from the host (PST_FAULT_INJECT,
+    read once per process, so in a child): the tree builds, the plan's
+    upload fails with PST_E_OOM and a message, and the process then plans
+    and decodes normally."""
+    import os
+    import subprocess
+
+    code = """
+import sys
+sys.path.insert(0, {root!r})
+import torch, numpy as np
+import prefix_shared_tree_amd as pst, workloads
+spec = workloads.config("1")
+q, k, v = workloads.make_tensors(spec, "cuda")
+tree = pst.Tree.from_spec(spec, out_dtype="f32")          # allocation 1
+try:
+    pst.Plan(tree)                                         # allocation 2: injected failure
+    print("NO-ERROR")
+except pst.PstError as e:
+    print("ERR", e.code, str(e))
+plan = pst.Plan(tree)                                      # allocation 3
+out, lse = pst.decode_attn(plan, q, k, v)
+torch.cuda.synchronize()
+print("OK", float(out.abs().sum()) > 0)
+""".format(root=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    env = dict(os.environ, PST_FAULT_INJECT="alloc:2")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=100)
+    say(r.stdout.strip())
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "ERR PST_E_OOM" in r.stdout and "injected device allocation failure" in r.stdout
+    assert "OK True" in r.stdout
+
+
 def test_max_rows_split():
     """More rows than one workgroup holds: the planner cuts row groups (> 256 rows)."""
     lens = [700] + [3] * 20
