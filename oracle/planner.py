@@ -31,7 +31,7 @@ reading taken here, implemented identically in the library, all in integers:
    lo = max_i C(rows_i, min(n_i, G)) and hi = sum_i cost(i, 1).
 6. ub_i = min(bmax_i, max(1, ceil(C(rows_i, n_i) / cost_l))).
 7. grid search k = 0..K: T_k = cost_l + (cost_l k) // K, b_i = min(ub_i, b_i(T_k));
-   7b (this build's addition): then one candidate per uniform piece length
+   7b (an addition to the pages' procedure): one candidate per uniform piece length
    U = G x 1, 2, 3, 4, 6, 8, 12, 16, ... (every node cut into pieces of U,
    the last shorter), up to the first U that holds the longest node, as
    k = K+1, K+2, ...; for every candidate the pieces (per row group) are

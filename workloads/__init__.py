@@ -388,7 +388,7 @@ def page_pools(spec: TreeSpec, k, v, page_size: int, *, spare_pages: int = 0, fi
 # Tree shapes of the CoDec evaluation (binary 2T ... 5-ary 5T and a degenerate
 # tree DT; CoDec page, 实验结果 section 1).  The page names the shapes and
 # sweeps sequence length, batch and shared-prefix ratio without printing the
-# trees, so the sizes below are this build's reading: every query's path holds
+# trees, so the sizes below are a reading of them: every query's path holds
 # `path_len` tokens, the root `shared` of them, the rest split evenly over
 # the deeper levels; one query per leaf.
 # ---------------------------------------------------------------------------
