@@ -398,6 +398,7 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": statistics.median(step_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
