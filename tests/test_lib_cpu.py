@@ -447,6 +447,7 @@ def test_flatten_options_and_growth():
     _raises("PST_E_INVALID_ARG", pst.Plan, t, num_bins=4, flatten=192, host_only=True)  # not a multiple of 128
     _raises("PST_E_INVALID_ARG", pst.Plan, t, num_bins=4, flatten=256, no_split=True, host_only=True)
     _raises("PST_E_INVALID_ARG", pst.Plan, t, num_bins=4, flatten=256, query_guided=True, host_only=True)
+    _raises("PST_E_UNSUPPORTED", pst.Plan, t, num_bins=4, flatten=128 * 1024, host_only=True)  # masks exceed 8 KB
     p = pst.Plan(t, num_bins=4, flatten=256, host_only=True)
     before = t.index()["visible"].copy()
     longer = spec.kv_len.copy()
