@@ -328,9 +328,11 @@ __device__ __forceinline__ void issue_tile(const PacParams& p, const TaskInfo& t
     }
     return;
   }
-  if (p.page_shift >= 0 && (1 << p.page_shift) < G::TT) {
-    // Pages shorter than a tile: consecutive blocks per wavefront, sharing
-    // one page number when a page holds their tokens (see issue_half).
+  if (p.page_shift >= 0 && ((1 << p.page_shift) < G::TT || (t.kv_begin & (G::TT - 1)) != 0)) {
+    // Pages shorter than a tile, or a piece that starts off a tile boundary
+    // of its node (64-token piece starts with 128-token tiles), so that a
+    // tile may cross a page: consecutive blocks per wavefront, sharing one
+    // page number when a page holds their tokens (see issue_half).
     const bool shared = (1 << p.page_shift) >= KB * TPB;
     PagedBlock pw{};
     if (shared) pw = paged_block(p, t, tok_base, w, KB * TPB);
@@ -352,7 +354,7 @@ __device__ __forceinline__ void issue_tile(const PacParams& p, const TaskInfo& t
   const char* kb = t.kbase + tok_base * stb;
   const char* vb = t.vbase + tok_base * stb;
   if (p.page_shift >= 0) {
-    // Pages of at least a tile: the tile lies in one page.
+    // Pages of at least a tile and a tile-aligned piece: the tile lies in one page.
     const PagedBlock pb = paged_block(p, t, tok_base, 0, 1);
     kb = t.kbase + pb.row * stb;
     vb = t.vbase + pb.row * stb;
@@ -444,8 +446,9 @@ __device__ __forceinline__ void issue_half(const PacParams& p, const TaskInfo& t
     }
     return;
   }
-  if (p.page_shift >= 0 && (1 << p.page_shift) < G::TT) {
-    // Pages shorter than a tile: this wavefront takes the consecutive blocks
+  if (p.page_shift >= 0 && ((1 << p.page_shift) < G::TT || (t.kv_begin & (G::TT - 1)) != 0)) {
+    // Pages shorter than a tile, or a piece that starts off a tile boundary
+    // of its node (so a tile may cross a page): this wavefront takes the consecutive blocks
     // kHalfOps w .. kHalfOps w + kHalfOps - 1, which share one page when a
     // page holds at least their tokens (one page number and one descriptor),
     // else each block looks up its own.
@@ -477,8 +480,8 @@ __device__ __forceinline__ void issue_half(const PacParams& p, const TaskInfo& t
   }
   const char* tbase = base + tok_base * stb;
   if (p.page_shift >= 0) {
-    // Pages of at least a tile: the tile lies in one page (tiles start at
-    // multiples of 64 tokens of the node), so one page number serves it.
+    // Pages of at least a tile and a piece that starts on a tile boundary:
+    // the tile lies in one page, so one page number serves it.
     const PagedBlock pb = paged_block(p, t, tok_base, 0, 1);
     tbase = base + pb.row * stb;
   }

@@ -190,6 +190,24 @@ def test_paged_kv(case):
     check(spec, (q, k, v), out, lse)
 
 
+@pytest.mark.parametrize("P", [128, 256, 1024])
+@pytest.mark.parametrize("dot_small", [False, True])
+def test_paged_tiles_off_page_boundaries(P, dot_small):
+    """Head dim 64 (128-token tiles) over pages of at least a tile, with
+    pieces of 192 tokens: pieces start at 64 mod 128, so their tiles straddle
+    page boundaries and must take the per-block page lookups."""
+    spec = workloads.random_tree(2500 + P, max_nodes=6, max_len=1500, min_len=300, max_queries=12,
+                                 num_q_heads=8, num_kv_heads=2, head_dim=64, dtype="bf16")
+    q, k, v = workloads.make_tensors(spec, "cuda")
+    paged, kp, vp = workloads.page_pools(spec, k, v, P, spare_pages=1)
+    tree = pst.Tree.from_paged(spec, paged, out_dtype="f32")
+    plan = pst.Plan(tree, num_bins=5, fixed_chunk=192, dot_small=dot_small)
+    assert any(int(t[2]) % 128 == 64 for t in plan.view()["tasks"])
+    out, lse = pst.decode_attn(plan, q, kp, vp)
+    torch.cuda.synchronize()
+    check(spec, (q, k, v), out, lse)
+
+
 @pytest.mark.parametrize("name,P", [("2", 16), ("4", 8)])
 def test_paged_config_sampled(name, P):
     """A full workload over a paged pool (document QA; masked speculative drafts), sampled queries."""
