@@ -351,8 +351,9 @@ print("OK", float(out.abs().sum()) > 0)
 @pytest.mark.parametrize("seed", range(64))
 def test_random_configurations(seed):
     """Random combinations of dtype, GQA group, head dim, tree shape, masked
-    nodes, paged pools, bin count, dot path and partition (cost model, fixed
-    chunks, flattened), all queries against the oracle."""
+    nodes, paged pools, bin count, row cap, dot path and partition (cost
+    model, fixed or odd chunks, one piece per node, flattened), all queries
+    against the oracle."""
     rng = np.random.default_rng(10000 + seed)
     dtype = "f32" if rng.random() < 0.25 else "bf16"
     hkv = int(rng.choice([1, 2, 4]))
@@ -363,7 +364,7 @@ def test_random_configurations(seed):
                                  num_q_heads=hkv * g, num_kv_heads=hkv, head_dim=d, dtype=dtype,
                                  masked_prob=float(rng.choice([0.0, 0.3])))
     q, k, v = workloads.make_tensors(spec, "cuda")
-    P = int(rng.choice([0, 0, 8, 16, 64, 256]))
+    P = int(rng.choice([0, 0, 8, 16, 64, 128, 256, 512]))
     if P:
         paged, kk, vv = workloads.page_pools(spec, k, v, P, spare_pages=int(rng.integers(0, 2)))
         tree = pst.Tree.from_paged(spec, paged, out_dtype="f32")
@@ -371,11 +372,15 @@ def test_random_configurations(seed):
         kk, vv = k, v
         tree = pst.Tree.from_spec(spec, out_dtype="f32")
     kw = dict(num_bins=int(rng.choice([0, 1, 3, 7, 32])), dot_small=bool(rng.random() < 0.3))
+    if dtype == "bf16" and g <= 32 and rng.random() < 0.25:
+        kw["max_rows"] = int(rng.choice([32, 64, 128]))
     u = rng.random()
     if u < 0.2:
-        kw["fixed_chunk"] = int(rng.choice([64, 128, 512]))
+        kw["fixed_chunk"] = int(rng.choice([64, 128, 192, 320, 512]))
     elif u < 0.45:
-        kw["flatten"] = int(rng.choice([128, 256, 640]))
+        kw["flatten"] = int(rng.choice([128, 256, 384, 640]))
+    elif u < 0.55:
+        kw["no_split"] = True
     say(f"seed {seed}: {dtype} H {hkv * g}/{hkv} d {d} N {spec.num_nodes} B {spec.num_queries} page {P} {kw}")
     plan = pst.Plan(tree, **kw)
     out, lse = pst.decode_attn(plan, q, kk, vv)
