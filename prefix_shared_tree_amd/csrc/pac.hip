@@ -1310,12 +1310,18 @@ template <typename T, int D, int LAYOUT>
 int launch_layout(const PacParams& p, void* stream) {
   const int grid = p.num_bins * p.hkv;
   constexpr size_t lds = LAYOUT == kFlat ? kLdsBytesFlat : kLdsBytes;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pac_kernel<T, D, LAYOUT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  // The dynamic-LDS limit is raised once per device (the attribute is per
+  // device); a race between two threads only sets it twice.
+  constexpr int kMaxDevices = 64;
+  static bool configured[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (dev < 0 || dev >= kMaxDevices || !configured[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pac_kernel<T, D, LAYOUT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return static_cast<int>(e);
-    configured = true;
+    if (dev >= 0 && dev < kMaxDevices) configured[dev] = true;
   }
   hipLaunchKernelGGL((pac_kernel<T, D, LAYOUT>), dim3(grid), dim3(kWaves<T> * 64), lds,
                      static_cast<hipStream_t>(stream), p);
