@@ -190,6 +190,39 @@ def test_paged_kv(case):
     check(spec, (q, k, v), out, lse)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_paged_pages_example(dtype):
+    """The shared-prefix blog's paged layout (section 4.3; tests/golden): the
+    96-token prefix in pages 0-5, the suffixes in pages 6 and 7 of a 16-token
+    page pool, one decode query per request."""
+    import json
+    import os
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    with open(os.path.join(root, "tests", "golden", "flashinfer_paged_prefix_96_4_4.json")) as f:
+        g = json.load(f)
+    tr, P = g["tree"], g["page_size"]
+    lens = np.array(tr["kv_len"])
+    spec = workloads.TreeSpec("pages-example", np.array(tr["parent"]), lens, np.concatenate([[0], np.cumsum(lens)[:-1]]),
+                              np.array(tr["query_node"]), 8, 2, 128, dtype, 43)
+    q, k, v = workloads.make_tensors(spec, "cuda")
+    # The pool as the page lays it out: node i's token j at page_idx[page_ptr[i] + j // P] * P + j % P.
+    kp = torch.full((2, 8 * P, 128), float("nan"), dtype=k.dtype, device="cuda")
+    vp = torch.full_like(kp, float("nan"))
+    for i in range(3):
+        for j in range(int(lens[i])):
+            row = tr["page_idx"][tr["page_ptr"][i] + j // P] * P + j % P
+            kp[:, row] = k[:, int(spec.kv_offset[i]) + j]
+            vp[:, row] = v[:, int(spec.kv_offset[i]) + j]
+    tree = pst.Tree(tr["parent"], None, tr["kv_len"], tr["query_node"], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    dtype=dtype, out_dtype="f32", page_size=P, page_ptr=tr["page_ptr"], page_idx=tr["page_idx"])
+    for kw in ({}, {"flatten": 128}):
+        plan = pst.Plan(tree, num_bins=2, **kw)
+        out, lse = pst.decode_attn(plan, q, kp, vp)
+        torch.cuda.synchronize()
+        check(spec, (q, k, v), out, lse)
+
+
 @pytest.mark.parametrize("P", [128, 256, 1024])
 @pytest.mark.parametrize("dot_small", [False, True])
 def test_paged_tiles_off_page_boundaries(P, dot_small):

@@ -456,3 +456,34 @@ def test_flatten_options_and_growth():
     p.free()
     t.set_lengths(longer)  # allowed again
     t.free()
+
+
+def test_paged_block_tables_of_the_pages_example():
+    """The shared-prefix blog's paged example (section 4.3, tests/golden): a
+    96-token prefix in pages 0-5 and two 4-token suffixes in pages 6 and 7.
+    The per-request block tables, their indptr, last-page lengths and every
+    token's pool row follow from the tree's page table and the query paths."""
+    import json
+
+    with open(os.path.join(ROOT, "tests", "golden", "flashinfer_paged_prefix_96_4_4.json")) as f:
+        g = json.load(f)
+    tr, P = g["tree"], g["page_size"]
+    t = pst.Tree(tr["parent"], None, tr["kv_len"], tr["query_node"], num_q_heads=4, num_kv_heads=1, head_dim=64,
+                 dtype="f32", page_size=P, page_ptr=tr["page_ptr"], page_idx=tr["page_idx"], host_only=True)
+    ix = t.index()
+    assert ix["visible"].tolist() == g["expect"]["visible"]
+    tables, last = [], []
+    for r in range(len(tr["query_node"])):
+        path = ix["qn_idx"][ix["qn_ptr"][r]:ix["qn_ptr"][r + 1]]
+        pages = [int(p) for i in path for p in ix["page_idx"][ix["page_ptr"][i]:ix["page_ptr"][i + 1]]]
+        tables.append(pages)
+        last.append(int(tr["kv_len"][path[-1]]) % P or P)
+        # Token j of the request's sequence: pool row from the block table
+        # (the page's view) equals the row through the node that holds it.
+        rows_block = [pages[j // P] * P + j % P for j in range(int(ix["visible"][r]))]
+        rows_tree = [int(ix["page_idx"][ix["page_ptr"][i] + j // P]) * P + j % P
+                     for i in path for j in range(int(tr["kv_len"][i]))]
+        assert rows_block == rows_tree
+    assert [0] + list(np.cumsum([len(x) for x in tables])) == g["expect"]["paged_kv_indptr"]
+    assert [p for x in tables for p in x] == g["expect"]["paged_kv_indices"]
+    assert last == g["expect"]["paged_kv_last_page_len"]
