@@ -113,3 +113,79 @@ def test_tree_attention_is_attention_over_the_visible_sequence(spec, seed):
             w = np.exp(s - s.max())
             assert np.allclose(O[r, h], (w @ v[kv, rows]) / w.sum(), rtol=0, atol=1e-12)
             assert np.isclose(L[r, h], s.max() + np.log(w.sum()), rtol=0, atol=1e-12)
+
+
+@settings(max_examples=40, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
+@given(st.lists(st.tuples(st.sampled_from("abp"), st.integers(0, 1000), st.integers(1, 3)), min_size=1, max_size=14))
+def test_decode_session_random_operations(ops):
+    """Random appends, forks and finishes on a host-only decode session, each
+    followed by the full consistency check against a node model (tree arrays,
+    every token's pool row, page accounting, index and plan bit-exact)."""
+    import torch
+
+    from prefix_shared_tree_amd.decode_loop import DecodeSession
+    from test_lib_cpu import _session_model_check
+
+    P, max_new = 8, 16
+    parent = np.array([-1, 0, 0])
+    lens = np.array([30, 5, 12])
+    off = np.array([0, 30, 35])
+    spec = workloads.TreeSpec("session", parent, lens, off, np.array([1, 2]), 4, 2, 64, "f32", 0)
+    T = int(lens.sum())
+    ids = torch.arange(1, T + 1, dtype=torch.float32)
+    k = torch.zeros((2, T, 64))
+    v = torch.zeros((2, T, 64))
+    k[:, :, 0] = ids
+    v[:, :, 3] = -ids
+    cm_lib, cm_or = pst.CostModel(ROWS, LENS, TABLE), oracle.CostTable(ROWS, LENS, TABLE)
+    sess = DecodeSession(spec, k, v, page_size=P, max_new_tokens=max_new, extra_pages=60, host_only=True,
+                         plan_kw=dict(cost=cm_lib, num_bins=5, max_rows=16))
+    nodes = [[int(parent[i]), list(range(int(off[i]) + 1, int(off[i] + lens[i]) + 1)), True] for i in range(3)]
+    queries = [1, 2]
+    nxt, appends = T + 1, 0
+    _session_model_check(sess, nodes, queries, P, cm_or)
+    for op, x, n in ops:
+        B = len(queries)
+        planned = True
+        if op == "a":
+            if appends >= max_new - 1:
+                continue
+            kn, vn = torch.zeros((B, 2, 64)), torch.zeros((B, 2, 64))
+            for r, mnode in enumerate(queries):
+                kn[r, :, 0], vn[r, :, 3] = nxt, -nxt
+                nodes[mnode][1].append(nxt)
+                nxt += 1
+            sess.append(kn, vn)
+            appends += 1
+            planned = False
+        elif op == "b":
+            qi = x % B
+            kn, vn = torch.zeros((n, 2, 64)), torch.zeros((n, 2, 64))
+            new = []
+            for j in range(n):
+                kn[j, :, 0], vn[j, :, 3] = nxt, -nxt
+                nodes.append([queries[qi], [nxt], True])
+                new.append(len(nodes) - 1)
+                nxt += 1
+            try:
+                sess.branch(qi, kn, vn)
+            except ValueError:  # pool exhausted: nothing changed
+                del nodes[-n:]
+                nxt -= n
+                continue
+            queries[qi] = new[0]
+            queries += new[1:]
+        else:
+            if B < 2:
+                continue
+            qi = x % B
+            del queries[qi]
+            live = set()
+            for mnode in queries:
+                while mnode >= 0:
+                    live.add(mnode)
+                    mnode = nodes[mnode][0]
+            for i, nd in enumerate(nodes):
+                nd[2] = nd[2] and i in live
+            sess.prune(qi)
+        _session_model_check(sess, nodes, queries, P, cm_or, planned=planned)
