@@ -487,3 +487,13 @@ def test_paged_block_tables_of_the_pages_example():
     assert [0] + list(np.cumsum([len(x) for x in tables])) == g["expect"]["paged_kv_indptr"]
     assert [p for x in tables for p in x] == g["expect"]["paged_kv_indices"]
     assert last == g["expect"]["paged_kv_last_page_len"]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with a message, before touching a device."""
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
