@@ -92,6 +92,17 @@ def test_config5_mqa_sampled():
     check(spec, t, out, lse, queries=sample(spec.num_queries, 24, 2))
 
 
+def test_config5_mha_sampled():
+    """The largest workload (MHA 32/32, ~38 GB of K/V: pool offsets beyond
+    2^32 bytes), in the launch configuration the bench times, on sampled
+    queries (every head)."""
+    spec = workloads.config("5-mha")
+    say(f"config 5-mha: {spec.name}, {spec.total_tokens} tokens")
+    t, plan, out, lse = run(spec)
+    check(spec, t, out, lse, queries=sample(spec.num_queries, 8, 4))
+    del t
+
+
 @pytest.mark.parametrize("seed", range(24))
 def test_random_trees(seed):
     """Random forests spanning the dot-product / matrix-core switch (rows 1..300)."""
