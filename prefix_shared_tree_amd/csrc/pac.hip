@@ -422,6 +422,17 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2_scaled(uint32_t w) {
 __device__ __forceinline__ char* kslot(int j) { return pac_lds + (j % NSTAGE) * STAGE_BYTES; }
 __device__ __forceinline__ char* vslot(int j) { return pac_lds + (j % NSTAGE) * STAGE_BYTES + TILE_BYTES; }
 
+// Which 1 KB blocks of a K or V half a wavefront's DMA fills: runs of
+// kHalfOps consecutive blocks per wavefront when each block finds its own
+// rows (flattened chunks; paged tiles that may cross a page), else
+// round-robin over the wavefronts.  Wave-uniform.
+template <int D>
+__device__ __forceinline__ bool half_in_runs(const PacParams& p, const TaskInfo& t) {
+  using G = Geo<D, 2>;
+  return (p.mask_words > 0 && !t.linear) ||
+         (p.page_shift >= 0 && ((1 << p.page_shift) < G::TT || (t.kv_begin & (G::TT - 1)) != 0));
+}
+
 // DMA of the K (or V) half of tile `tile` (16 KB) into `dst`: every wavefront
 // writes kHalfOps 1 KB blocks; lane L of block b fills chunk position
 // P = 64 b + L, i.e. token P / CPT, chunk (P % CPT) ^ (token % CPT).
@@ -446,7 +457,7 @@ __device__ __forceinline__ void issue_half(const PacParams& p, const TaskInfo& t
     }
     return;
   }
-  if (p.page_shift >= 0 && ((1 << p.page_shift) < G::TT || (t.kv_begin & (G::TT - 1)) != 0)) {
+  if (half_in_runs<D>(p, t)) {
     // Pages shorter than a tile, or a piece that starts off a tile boundary
     // of its node (so a tile may cross a page): this wavefront takes the consecutive blocks
     // kHalfOps w .. kHalfOps w + kHalfOps - 1, which share one page when a
@@ -841,14 +852,38 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     }
   };
 
+  // V of tile j to fp16 in place (scaled by kVScale): each lane converts the
+  // 16-byte chunks that its own DMA wrote, which its own wait has made
+  // visible to it, so no barrier is needed between the wait and the
+  // conversion.
+  auto convert_own_v = [&](int j) {
+    constexpr int KB = kHalfOps<NW>;
+    const bool runs = half_in_runs<D>(p, t);
+    uint4* vp[KB];
+    uint4 x[KB];
+#pragma unroll
+    for (int c = 0; c < KB; ++c) {
+      const int b = runs ? KB * w + c : c * NW + w;
+      vp[c] = reinterpret_cast<uint4*>(vslot(j) + b * 1024 + lane * 16);
+      x[c] = *vp[c];
+    }
+#pragma unroll
+    for (int c = 0; c < KB; ++c)
+      *vp[c] = make_uint4(bf16x2_to_f16x2_scaled(x[c].x), bf16x2_to_f16x2_scaled(x[c].y),
+                          bf16x2_to_f16x2_scaled(x[c].z), bf16x2_to_f16x2_scaled(x[c].w));
+  };
   // Start of iteration i (0 <= i <= nt): wait for group i (K of tile i, V of
-  // tile i - 1), barrier, issue group i + 3 into the halves finished in
-  // iteration i - 1; then either (i = 0) the queries into registers or (i > 0)
-  // the conversion of V of tile i - 1 to fp16, each thread its share; a
-  // second barrier publishes them (at i = 0 it frees the query stages, which
-  // group 3 then refills).
+  // tile i - 1); for i > 0 convert this lane's chunks of V of tile i - 1 to
+  // fp16; one barrier publishes both; issue group i + 3 into the halves
+  // finished in iteration i - 1.  At i = 0 the queries go into registers
+  // instead, and a second barrier frees their stages, which group 3 then
+  // refills.
   auto sync = [&](int i, bool refill) {
     wait_vmem_n(group_ops<NW>(i + 1, nt) + group_ops<NW>(i + 2, nt));
+    if (i > 0) {
+      convert_own_v(i - 1);
+      wait_lds_all();
+    }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");  // no LDS access moves above the barrier
     // K of tile i - 1 and V of tile i - 2 are finished: refill them (here, or
@@ -872,21 +907,9 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
           }
         }
       }
-    } else {
-      constexpr int CV = TILE_BYTES / (NW * 64) / 16;  // 16-byte chunks per thread
-      uint4* vp = reinterpret_cast<uint4*>(vslot(i - 1) + tid * CV * 16);
-      uint4 x[CV];
-#pragma unroll
-      for (int c = 0; c < CV; ++c) x[c] = vp[c];
-#pragma unroll
-      for (int c = 0; c < CV; ++c)
-        vp[c] = make_uint4(bf16x2_to_f16x2_scaled(x[c].x), bf16x2_to_f16x2_scaled(x[c].y),
-                           bf16x2_to_f16x2_scaled(x[c].z), bf16x2_to_f16x2_scaled(x[c].w));
-    }
-    wait_lds_all();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (i == 0) {
+      wait_lds_all();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
       if (3 < nt) issue_half<D, NW>(p, t, t.kbase, stb, 3, kslot(3), tid);
       if (2 < nt) issue_half<D, NW>(p, t, t.vbase, stb, 2, vslot(2), tid);
     }
