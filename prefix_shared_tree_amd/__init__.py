@@ -2,7 +2,7 @@
 
 Argument marshalling only.  Every step of the computation (index, plan, the
 partial-attention and reduction kernels) runs in the native library built
-from ``csrc/`` (``python -m prefix_shared_tree_amd.build``).  If the library
+from ``csrc/`` (``python prefix_shared_tree_amd/build.py``).  If the library
 is missing, importing this package raises: there is no fallback.
 
     import prefix_shared_tree_amd as pst
@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libpst.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m prefix_shared_tree_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python prefix_shared_tree_amd/build.py` "
         "(the HIP library is required; there is no fallback path)")
 
 # libpst.so links against libamdhip64.so.7.  PyTorch ships its own HIP
