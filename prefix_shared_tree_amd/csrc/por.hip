@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "pst_internal.h"
 
@@ -29,11 +30,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
 // Grid: (query, chunk of kPorThreads (head, 4-channel) pairs).  One pass over
-// the chain in batches of kBatch slots: all loads of a batch are in flight
-// together, then the batch is folded into the running (max, sum, O) at the
-// batch maximum (the binary merge applied kBatch times at once).  The slot
-// range is uniform over the workgroup, so the tail batch re-reads a valid
-// slot instead of branching and gives it weight 0.
+// the chain in batches: all loads of a batch are in flight together, then the
+// batch is folded into the running (max, sum, O) at the batch maximum (the
+// binary merge applied to the whole batch at once).  Full batches take 8
+// slots; the tail (fewer than 8) is one batch of 8, 4, 2 or 1 slots whose
+// unused entries are not loaded and get weight 0.  The slot range is
+// uniform over the workgroup, so these choices are scalar branches.
 constexpr int kBatch = 8;
 template <int D, bool BF16_OUT>
 __global__ __launch_bounds__(kPorThreads) void por_kernel(PorParams p, int chunks) {
@@ -46,18 +48,23 @@ __global__ __launch_bounds__(kPorThreads) void por_kernel(PorParams p, int chunk
   const int h = idx / C4, c4 = idx % C4;
   float m = kNegInf, z = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int64_t s = s0; s < s1; s += kBatch) {
-    float lse[kBatch];
-    float4 x[kBatch];
+  // Fold slots [s, s + n) (n <= NB) into the running state.
+  auto fold = [&](auto nb_tag, int64_t s, int n) {
+    constexpr int NB = decltype(nb_tag)::value;
+    float lse[NB];
+    float4 x[NB];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int64_t sj = s + j < s1 ? s + j : s0;
-      lse[j] = s + j < s1 ? p.lsepart[sj * p.hq + h] : kNegInf;
-      x[j] = *reinterpret_cast<const float4*>(p.opart + (sj * p.hq + h) * D + c4 * 4);
+    for (int j = 0; j < NB; ++j) {
+      lse[j] = kNegInf;
+      x[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < n) {
+        lse[j] = p.lsepart[(s + j) * p.hq + h];
+        x[j] = *reinterpret_cast<const float4*>(p.opart + ((s + j) * p.hq + h) * D + c4 * 4);
+      }
     }
     float bm = lse[0];
 #pragma unroll
-    for (int j = 1; j < kBatch; ++j) bm = fmaxf(bm, lse[j]);
+    for (int j = 1; j < NB; ++j) bm = fmaxf(bm, lse[j]);
     const float mn = fmaxf(m, bm);
     const float mref = mn == kNegInf ? 0.f : mn;
     const float a = __builtin_amdgcn_exp2f((m - mref) * kLog2e);  // 0 while m is -inf
@@ -67,7 +74,7 @@ __global__ __launch_bounds__(kPorThreads) void por_kernel(PorParams p, int chunk
     acc.z *= a;
     acc.w *= a;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const float wgt = __builtin_amdgcn_exp2f((lse[j] - mref) * kLog2e);
       const bool live = wgt > 0.f;  // an empty partial's O may be anything
       z += wgt;
@@ -77,7 +84,18 @@ __global__ __launch_bounds__(kPorThreads) void por_kernel(PorParams p, int chunk
       acc.w += live ? wgt * x[j].w : 0.f;
     }
     m = mn;
-  }
+  };
+  int64_t s = s0;
+  for (; s + kBatch <= s1; s += kBatch) fold(std::integral_constant<int, kBatch>{}, s, kBatch);
+  const int rem = static_cast<int>(s1 - s);
+  if (rem > 4)
+    fold(std::integral_constant<int, 8>{}, s, rem);
+  else if (rem > 2)
+    fold(std::integral_constant<int, 4>{}, s, rem);
+  else if (rem == 2)
+    fold(std::integral_constant<int, 2>{}, s, 2);
+  else if (rem == 1)
+    fold(std::integral_constant<int, 1>{}, s, 1);
   const float inv = z > 0.f ? 1.f / z : 0.f;
   const int64_t o = (static_cast<int64_t>(r) * p.hq + h) * D + c4 * 4;
   if (BF16_OUT) {
