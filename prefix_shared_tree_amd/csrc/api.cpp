@@ -571,7 +571,8 @@ pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* op
         const int32_t* rows = p->r.flat_rows.data() + a.kv_begin;
         bool linear = true;
         for (int32_t k = 1; linear && k < a.kv_len; ++k) linear = rows[k] == rows[0] + k;
-        b.flags = (all_seen ? 0 : kDevMasked) | (linear ? kDevLinear : 0);
+        const int64_t chunk_rows = static_cast<int64_t>(p->r.flat_ptr[a.node + 1] - p->r.flat_ptr[a.node]) * g;
+        b.flags = (all_seen ? 0 : kDevMasked) | (linear ? kDevLinear : 0) | (a.row_count < chunk_rows ? kDevShared : 0);
         b.row0 = linear ? rows[0] : 0;
         continue;
       }
@@ -584,7 +585,9 @@ pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* op
       b.row_begin = a.row_begin;
       b.row_count = a.row_count;
       b.piece = a.piece;
-      b.flags = ((a.flags & PST_TASK_LAST_PIECE) ? kDevLast : 0) | (t->ix.masked[a.node] ? kDevMasked : 0);
+      const int64_t node_rows = static_cast<int64_t>(t->ix.nq_ptr[a.node + 1] - t->ix.nq_ptr[a.node]) * g;
+      b.flags = ((a.flags & PST_TASK_LAST_PIECE) ? kDevLast : 0) | (t->ix.masked[a.node] ? kDevMasked : 0) |
+                (a.row_count < node_rows ? kDevShared : 0);
       b.row0 = 0;
     }
     DevArena arena;

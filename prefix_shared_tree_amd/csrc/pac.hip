@@ -131,19 +131,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, in
 // Written as inline assembly so the compiler does not see an LDS store in
 // flight: it would otherwise wait for every outstanding DMA before each LDS
 // read.  The tile loop waits explicitly (wait_vmem) for the tile it reads.
-// M0 carries the destination and is restored afterwards.
+// M0 carries the destination and is restored afterwards.  NT: the load
+// carries the non-temporal hint (K/V read by one task only: streamed past
+// the caches instead of displacing lines that are still to be read).
+template <bool NT = false>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, uint32_t lds_addr) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-      : "memory");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen nt lds\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+        : "memory");
 }
 // threadIdx.x through an opaque move: values derived from it inside a piece
 // are recomputed per piece instead of being hoisted out of the piece loop and
@@ -211,6 +226,7 @@ struct TaskInfo {
   int piece, kv_begin, kv_len, row_begin, row_count, e0, masked, node;
   int flat0;          // flattened chunk: its first token in the row table
   int linear;         // flattened chunk over consecutive pool rows: addressed like a contiguous run
+  int shared;         // other tasks (row groups, query-guided groups) read the same K/V tokens
   const char* kbase;  // K of this kv head at the piece's first token (paged: at the pool's first row)
   const char* vbase;
 };
@@ -436,7 +452,7 @@ __device__ __forceinline__ bool half_in_runs(const PacParams& p, const TaskInfo&
 // DMA of the K (or V) half of tile `tile` (16 KB) into `dst`: every wavefront
 // writes kHalfOps 1 KB blocks; lane L of block b fills chunk position
 // P = 64 b + L, i.e. token P / CPT, chunk (P % CPT) ^ (token % CPT).
-template <int D, int NW>
+template <int D, int NW, bool NT>
 __device__ __forceinline__ void issue_half(const PacParams& p, const TaskInfo& t, const char* base, int64_t stb,
                                            int tile, char* dst, int tid) {
   using G = Geo<D, 2>;
@@ -453,7 +469,7 @@ __device__ __forceinline__ void issue_half(const PacParams& p, const TaskInfo& t
 #pragma unroll
     for (int c = 0; c < KB; ++c) {
       const int b = KB * w + c;
-      dma16(r, flat_voff<G::CPT, TPB>(rw + c * TPB, b, lane, stb), lds_addr(dst + b * 1024));
+      dma16<NT>(r, flat_voff<G::CPT, TPB>(rw + c * TPB, b, lane, stb), lds_addr(dst + b * 1024));
     }
     return;
   }
@@ -472,7 +488,7 @@ __device__ __forceinline__ void issue_half(const PacParams& p, const TaskInfo& t
         const int b = KB * w + c;
         const int P = b * 64 + lane;
         const int tok = P / G::CPT, phys = P % G::CPT;
-        dma16(r, static_cast<int>((tok - KB * w * TPB) * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4),
+        dma16<NT>(r, static_cast<int>((tok - KB * w * TPB) * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4),
               lds_addr(dst + b * 1024));
       }
     } else {
@@ -483,7 +499,7 @@ __device__ __forceinline__ void issue_half(const PacParams& p, const TaskInfo& t
         const __amdgpu_buffer_rsrc_t r = make_rsrc(base + pb.row * stb, pb.valid * stb);
         const int P = b * 64 + lane;
         const int tok = P / G::CPT, phys = P % G::CPT;
-        dma16(r, static_cast<int>((tok - b * TPB) * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4),
+        dma16<NT>(r, static_cast<int>((tok - b * TPB) * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4),
               lds_addr(dst + b * 1024));
       }
     }
@@ -503,7 +519,7 @@ __device__ __forceinline__ void issue_half(const PacParams& p, const TaskInfo& t
     const int b = c * NW + w;
     const int P = b * 64 + lane;
     const int tok = P / G::CPT, phys = P % G::CPT;
-    dma16(r, static_cast<int>(tok * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4), lds_addr(dst + b * 1024));
+    dma16<NT>(r, static_cast<int>(tok * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4), lds_addr(dst + b * 1024));
   }
 }
 
@@ -525,7 +541,7 @@ __device__ __forceinline__ int group_ops(int j, int nt) {
 // sub-steps are software-pipelined: step k computes S = K Q^T and the
 // softmax of step k while the matrix cores run O += P V of step k - 1, so
 // matrix-core and vector work overlap inside a wavefront.
-template <int D, int RBR, int TS, int NW>
+template <int D, int RBR, int TS, int NW, bool NT>
 __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t, int kvh) {
   using G = Geo<D, 2>;
   constexpr int KS = D / 32;  // k-steps of S^T = K Q^T
@@ -590,11 +606,11 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
       if (o * NW + w < qops_total) dma16(rq, static_cast<int>(qoff[o]), lds_addr(qarea + (o * NW + w) * 1024));
   }
   if (p.mask_words > 0) issue_masks<NW>(p, t, tid);
-  if (0 < nt) issue_half<D, NW>(p, t, t.kbase, stb, 0, kslot(0), tid);
-  if (1 < nt) issue_half<D, NW>(p, t, t.kbase, stb, 1, kslot(1), tid);
-  if (0 < nt) issue_half<D, NW>(p, t, t.vbase, stb, 0, vslot(0), tid);
-  if (2 < nt) issue_half<D, NW>(p, t, t.kbase, stb, 2, kslot(2), tid);
-  if (1 < nt) issue_half<D, NW>(p, t, t.vbase, stb, 1, vslot(1), tid);
+  if (0 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, 0, kslot(0), tid);
+  if (1 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, 1, kslot(1), tid);
+  if (0 < nt) issue_half<D, NW, NT>(p, t, t.vbase, stb, 0, vslot(0), tid);
+  if (2 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, 2, kslot(2), tid);
+  if (1 < nt) issue_half<D, NW, NT>(p, t, t.vbase, stb, 1, vslot(1), tid);
 
   bf16x8 qf[RBR][KS];
   f32x4 o[DB][RBR];
@@ -692,8 +708,8 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
       // and eight wavefronts issuing together right after a barrier queue up
       // behind each other.  (Bandwidth-bound layouts refill at the barrier,
       // as early as possible.)
-      if (kSpread && sb == 0 && tile + 3 < nt) issue_half<D, NW>(p, t, t.kbase, stb, tile + 3, kslot(tile + 3), tid);
-      if (kSpread && sb == NSUB - 1 && tile + 2 < nt) issue_half<D, NW>(p, t, t.vbase, stb, tile + 2, vslot(tile + 2), tid);
+      if (kSpread && sb == 0 && tile + 3 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, tile + 3, kslot(tile + 3), tid);
+      if (kSpread && sb == NSUB - 1 && tile + 2 < nt) issue_half<D, NW, NT>(p, t, t.vbase, stb, tile + 2, vslot(tile + 2), tid);
       if constexpr (!kSpread) pv(vslot(tile - 1), ts, sb);
     }
     // Raw scores; lane holds tokens 4 lg + i of each 16-token block, row l16.
@@ -890,8 +906,8 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     // in the steps of tile i when `refill` is false; at i = 0 the refill
     // targets hold the queries: after the reads below).
     if (i > 0 && refill) {
-      if (i + 3 < nt) issue_half<D, NW>(p, t, t.kbase, stb, i + 3, kslot(i + 3), tid);
-      if (i + 2 < nt) issue_half<D, NW>(p, t, t.vbase, stb, i + 2, vslot(i + 2), tid);
+      if (i + 3 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, i + 3, kslot(i + 3), tid);
+      if (i + 2 < nt) issue_half<D, NW, NT>(p, t, t.vbase, stb, i + 2, vslot(i + 2), tid);
     }
     if (i == 0) {
       if (active) {
@@ -910,8 +926,8 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
       wait_lds_all();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (3 < nt) issue_half<D, NW>(p, t, t.kbase, stb, 3, kslot(3), tid);
-      if (2 < nt) issue_half<D, NW>(p, t, t.vbase, stb, 2, vslot(2), tid);
+      if (3 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, 3, kslot(3), tid);
+      if (2 < nt) issue_half<D, NW, NT>(p, t, t.vbase, stb, 2, vslot(2), tid);
     }
   };
   // The NSUB steps of tile i (tile 0: no products of a previous tile).
@@ -1297,6 +1313,7 @@ void pac_kernel(PacParams p) {
     t.node = __builtin_amdgcn_readfirstlane(task.node);
     t.flat0 = static_cast<int>(tok0);
     t.linear = (__builtin_amdgcn_readfirstlane(task.flags) & kDevLinear) != 0;
+    t.shared = (__builtin_amdgcn_readfirstlane(task.flags) & kDevShared) != 0;
     // Contiguous: K/V at the piece's first token; paged and flattened: the
     // head's pool start (blocks add their rows), or for a flattened chunk
     // over consecutive rows its first row.
@@ -1313,12 +1330,24 @@ void pac_kernel(PacParams p) {
       if (t.row_count >= p.mfma_min_rows) {
         // Slabs of 16 RBR rows, TS wavefronts per slab.
         static_assert(NW == 8, "row dispatch for 8 wavefronts");
-        if (t.row_count <= 32)
-          mfma_piece<D, 1, 2, NW>(p, t, kvh);
-        else if (t.row_count <= 128)
-          mfma_piece<D, 2, 2, NW>(p, t, kvh);
-        else
-          mfma_piece<D, 2, 1, NW>(p, t, kvh);
+        // Bandwidth-bound layouts stream K/V with the non-temporal hint
+        // unless other tasks read the same tokens (row groups, the
+        // query-guided baseline): those reads may still hit in L2.  The
+        // compute-bound layout (more than 128 rows, where the row groups
+        // are) keeps the default policy.
+        if (t.row_count <= 32) {
+          if (t.shared)
+            mfma_piece<D, 1, 2, NW, false>(p, t, kvh);
+          else
+            mfma_piece<D, 1, 2, NW, true>(p, t, kvh);
+        } else if (t.row_count <= 128) {
+          if (t.shared)
+            mfma_piece<D, 2, 2, NW, false>(p, t, kvh);
+          else
+            mfma_piece<D, 2, 2, NW, true>(p, t, kvh);
+        } else {
+          mfma_piece<D, 2, 1, NW, false>(p, t, kvh);
+        }
         done = true;
       }
     }

@@ -45,13 +45,14 @@ struct DevTask {
   int32_t row_begin;
   int32_t row_count;
   int32_t piece;
-  int32_t flags;    // kDevLast | kDevMasked | kDevLinear
+  int32_t flags;    // kDevLast | kDevMasked | kDevLinear | kDevShared
   int64_t row0;     // kDevLinear: pool row of the chunk's first token (its rows are consecutive)
 };
 static_assert(sizeof(DevTask) == 48, "device task layout");
 constexpr int32_t kDevLast = 1;
 constexpr int32_t kDevMasked = 2;  // the task needs the mask test (a masked node, a chunk whose masks are not all ones)
 constexpr int32_t kDevLinear = 4;  // flattened chunk over consecutive pool rows (addressed as a contiguous run)
+constexpr int32_t kDevShared = 8;  // another task (a row group of the same node or chunk) reads the same K/V tokens
 constexpr int32_t kMaskWordsMax = 1024;  // mask words of one flattened task (8 KB of LDS)
 
 struct CostModel {
