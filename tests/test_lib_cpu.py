@@ -497,3 +497,24 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_build_script_loads_without_the_package():
+    """build() must work on a fresh checkout, where the package refuses to
+    import because libpst.so does not exist yet: the build script is loaded
+    by path and imports nothing from the package."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import importlib.util, os, sys\n"
+        f"spec = importlib.util.spec_from_file_location('_b', os.path.join({root!r}, 'prefix_shared_tree_amd', 'build.py'))\n"
+        "m = importlib.util.module_from_spec(spec); spec.loader.exec_module(m)\n"
+        "assert callable(m.build)\n"
+        "assert 'prefix_shared_tree_amd' not in sys.modules\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd="/")
+    assert r.returncode == 0, r.stderr
+    src = open(os.path.join(root, "__graft_entry__.py")).read()
+    assert "spec_from_file_location" in src and "from prefix_shared_tree_amd.build" not in src
