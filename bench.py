@@ -223,11 +223,12 @@ def flatten_sweep(torch, pst, workloads, a):
         variants += [(f"node_chunk_{c}", {"fixed_chunk": c}) for c in chunks]
         variants += [(f"flatten_{c}", {"flatten": c}) for c in chunks]
         r = {"queries": spec.num_queries, "nodes": spec.num_nodes, "unique_kv_bytes": st["unique_kv_bytes"]}
-        # An untimed pass first: the first variant timed after the inputs
-        # were made otherwise reads up to 10 % slow.
+        # An untimed pass first (as many cold steps as each variant's
+        # warm-up): the first variant timed after the inputs were made
+        # otherwise reads up to 20 % slow.
         plan = pst.Plan(tree)
         ws = pst.workspace(plan)
-        time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, 3, 3)
+        time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, 3, a.warmup)
         del ws, plan
         for name, kw in variants:
             plan = pst.Plan(tree, **kw)
