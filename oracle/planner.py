@@ -26,7 +26,15 @@ reading taken here, implemented identically in the library, all in integers:
    piece k = [k Lp, min((k+1) Lp, n)); bmax = ceil(n/G).
 3. cost(i, b) = sum over row groups and pieces of C(rows, piece length).
 4. b_i(T) = the smallest b in [1, bmax] whose longest piece of the largest
-   row group costs <= T, else bmax.  W(T) = sum_i cost(i, b_i(T)).
+   row group costs <= T, else bmax.  W(T) = sum_i min over b in
+   [b_i(T), bmax_i] of cost(i, b): the least total cost of any splits whose
+   pieces all cost <= T (every b >= b_i(T) qualifies, the piece length
+   shrinking with b).  A makespan of T needs m T >= W(T) (the largest block
+   costs at least the average), so the smallest such T is the section's
+   lower bound cost_l; W is non-increasing in T, so the binary search finds
+   it.  (cost(i, b) is not monotone in b under every table: taking
+   cost(i, b_i(T)) alone made W jump up with T and the search miss the
+   smallest T.)
 5. cost_l = smallest T in [lo, hi] with m T >= W(T) by binary search, with
    lo = max_i C(rows_i, min(n_i, G)) and hi = sum_i cost(i, 1).
 6. ub_i = min(bmax_i, max(1, ceil(C(rows_i, n_i) / cost_l))).
@@ -146,8 +154,19 @@ def plan(index, kv_len, g, table, m, *, r_max=256, tile=64, grid_steps=8,
             lps[nd.i] = fixed_chunk if fixed_chunk > 0 else lp_for(nd, 1)
         candidates = [lps]
     else:
+        # Per node, the least cost over splits into b or more pieces:
+        # least[nd.i][b] = min over b' in [b, bmax] of cost(i, b').
+        least = {}
+        for nd in nodes:
+            suf = [0] * (nd.bmax + 2)
+            suf[nd.bmax + 1] = None
+            for b in range(nd.bmax, 0, -1):
+                c = _cost_with_lp(table, nd, lp_for(nd, b))
+                suf[b] = c if suf[b + 1] is None else min(c, suf[b + 1])
+            least[nd.i] = suf
+
         def W(T):
-            return sum(_cost_with_lp(table, nd, lp_for(nd, _b_of_T(table, nd, T, G))) for nd in nodes)
+            return sum(least[nd.i][_b_of_T(table, nd, T, G)] for nd in nodes)
 
         lo = max(table.lookup(nd.rpg, min(nd.n, G)) for nd in nodes)
         hi = sum(_cost_with_lp(table, nd, lp_for(nd, 1)) for nd in nodes)

@@ -17,7 +17,9 @@
 //    groups only when a node has more rows than a workgroup holds;
 //  * b pieces have Lp = roundup(ceil(n / b), G) tokens (the last shorter);
 //  * b(T) = smallest b whose longest piece of the largest row group costs
-//    <= T; W(T) = total cost at b(T); cost_l = smallest T with m T >= W(T);
+//    <= T; W(T) = the least total cost of splits into b(T) or more pieces
+//    per node (every such split has all pieces <= T); cost_l = smallest T
+//    with m T >= W(T) (W is non-increasing, so a binary search finds it);
 //  * candidates T_k = cost_l + cost_l * k / K (k = 0..K), b = min(ub, b(T_k));
 //  * pieces placed by longest-processing-time list scheduling (Graham 1966,
 //    cited by CoDec) onto the bin with the smallest (load, id); the
@@ -177,9 +179,22 @@ pst_status build_plan(const TreeIndex& ix, int32_t g, const CostModel& cost, con
     for (const PNode& nd : nodes) lps.push_back(o.fixed_chunk > 0 ? o.fixed_chunk : lp_of(nd.n, 1, G));
     candidates.push_back(lps);
   } else {
+    // least[a][b] = min over b' in [b, bmax] of cost(node a, b'): a makespan
+    // of T allows any split into b(T) or more pieces, so W(T), the least
+    // total work at T, takes the cheapest of them (cost is not monotone in b
+    // under every table).
+    std::vector<std::vector<int64_t>> least(nodes.size());
+    for (size_t a = 0; a < nodes.size(); ++a) {
+      const PNode& nd = nodes[a];
+      least[a].assign(nd.bmax + 2, 0);
+      for (int64_t b = nd.bmax; b >= 1; --b) {
+        const int64_t c = cost_with_lp(cost, nd, lp_of(nd.n, b, G));
+        least[a][b] = b == nd.bmax ? c : std::min(c, least[a][b + 1]);
+      }
+    }
     auto W = [&](int64_t T) {
       int64_t w = 0;
-      for (const PNode& nd : nodes) w += cost_with_lp(cost, nd, lp_of(nd.n, b_of_T(cost, nd, T, G), G));
+      for (size_t a = 0; a < nodes.size(); ++a) w += least[a][b_of_T(cost, nodes[a], T, G)];
       return w;
     };
     int64_t lo = 0, hi = 0;
