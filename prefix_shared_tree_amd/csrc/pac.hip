@@ -84,6 +84,9 @@ constexpr size_t kTileBytes = static_cast<size_t>(NSTAGE) * STAGE_BYTES;  // 128
 constexpr size_t kQOff = 2 * STAGE_BYTES + TILE_BYTES;
 constexpr size_t kAuxOff = kQOff + 64 * 1024;
 constexpr size_t kAuxBytes = 8 * 1024;  // softmax states exchanged between wavefronts; next task record
+// After the first 4 KB of the aux area (the softmax-state exchange uses at
+// most 4 KB): the largest |V| each wavefront converted in a piece.
+constexpr size_t kVexpOff = kAuxOff + 4096;
 constexpr size_t kLdsBytes = kAuxOff + kAuxBytes;
 // Flattened chunks add their bit causal masks (up to kMaskWordsMax words per
 // task) after the rest.
@@ -421,18 +424,32 @@ __device__ __forceinline__ void run_tiles(const PacParams& p, const TaskInfo& t,
 // O^T += V^T P^T runs in fp16: P <= 2^kLazy is rounded to nearest fp16
 // (2^-11 relative per weight, four times finer than bf16) and the row sums
 // add the same rounded P.  Each V tile is converted once in LDS, by all
-// threads together, from bf16 to fp16 scaled by 2^-8 (exact for |v| in
-// [2^-6, 2^23]; smaller values keep an absolute error below 2^-17, larger
-// ones saturate: round-toward-zero never overflows to infinity); the output
-// takes the 2^8 back when it is normalised.
-constexpr float kVScale = 0x1p-8f;
+// threads together, from bf16 to fp16 times 2^(15 - ev), with one exponent ev
+// per piece.  The piece is right for ev when its largest |v| has exponent E
+// in [ev - kEvWindow, ev]: then every |v| < 2^(ev + 1) lands below 2^16 (no
+// saturation), the largest lands at or above 2^(15 - kEvWindow), and bf16
+// values (8 significant bits) convert exactly down to 2^(ev - 29), keep 8
+// bits down to 2^(ev - 32) and below that carry an absolute error under
+// 2^(ev - 39) (round toward zero into fp16 subnormals): at least 2^26 below
+// the piece's largest |v| keeps bf16 precision.  Each lane keeps the largest
+// |v| it converts; at the piece's end the workgroup takes their maximum, and
+// if E fell outside the window the piece is computed once more with ev = E,
+// which fits by construction.  The next piece of the workgroup starts from
+// the last ev (plus headroom after a repeat), so a repeat happens only when
+// the V scale moves by more than the window between pieces.  The output takes
+// 2^(ev - 15) back when it is normalised.
+constexpr int kEvStart = 3;     // the first piece of a workgroup: |v| below 16
+constexpr int kEvWindow = 6;    // accepted E in [ev - kEvWindow, ev]
+constexpr int kEvMin = -100;    // ev never goes lower (nor is a piece of smaller |v| repeated for it)
+constexpr int kEvMax = 127;
+
+__device__ __forceinline__ float exp2i(int e) {  // 2^e for integer e in [-126, 127]
+  return __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+}
 
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   const f32x2 x = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
-}
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2_scaled(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(w) * kVScale, bf16_hi(w) * kVScale));
 }
 
 __device__ __forceinline__ char* kslot(int j) { return pac_lds + (j % NSTAGE) * STAGE_BYTES; }
@@ -541,8 +558,10 @@ __device__ __forceinline__ int group_ops(int j, int nt) {
 // sub-steps are software-pipelined: step k computes S = K Q^T and the
 // softmax of step k while the matrix cores run O += P V of step k - 1, so
 // matrix-core and vector work overlap inside a wavefront.
+// Returns false when the piece's V did not fit the scale it started from
+// (ev_carry then holds the scale to run it again with, `retry` true).
 template <int D, int RBR, int TS, int NW, bool NT>
-__device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t, int kvh) {
+__device__ __forceinline__ bool mfma_piece(const PacParams& p, const TaskInfo& t, int kvh, int& ev_carry, bool retry) {
   using G = Geo<D, 2>;
   constexpr int KS = D / 32;  // k-steps of S^T = K Q^T
   constexpr int DB = D / 16;  // d-blocks of O^T
@@ -868,10 +887,13 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     }
   };
 
-  // V of tile j to fp16 in place (scaled by kVScale): each lane converts the
-  // 16-byte chunks that its own DMA wrote, which its own wait has made
-  // visible to it, so no barrier is needed between the wait and the
-  // conversion.
+  // The piece's V scale (see above).
+  const int ev = ev_carry;
+  const float vs = exp2i(15 - ev);  // bf16 -> fp16 factor
+  float vmax = 0.f;           // largest |v| this lane has converted in the piece
+  // V of tile j to fp16 in place: each lane converts the 16-byte chunks that
+  // its own DMA wrote, which its own wait has made visible to it, so no
+  // barrier is needed between the wait and the conversion.
   auto convert_own_v = [&](int j) {
     constexpr int KB = kHalfOps<NW>;
     const bool runs = half_in_runs<D>(p, t);
@@ -883,10 +905,34 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
       vp[c] = reinterpret_cast<uint4*>(vslot(j) + b * 1024 + lane * 16);
       x[c] = *vp[c];
     }
+    float f[KB][8];
 #pragma unroll
-    for (int c = 0; c < KB; ++c)
-      *vp[c] = make_uint4(bf16x2_to_f16x2_scaled(x[c].x), bf16x2_to_f16x2_scaled(x[c].y),
-                          bf16x2_to_f16x2_scaled(x[c].z), bf16x2_to_f16x2_scaled(x[c].w));
+    for (int c = 0; c < KB; ++c) {
+      const uint32_t wv[4] = {x[c].x, x[c].y, x[c].z, x[c].w};
+      uint32_t h[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        f[c][2 * k] = bf16_lo(wv[k]);
+        f[c][2 * k + 1] = bf16_hi(wv[k]);
+        h[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[c][2 * k] * vs, f[c][2 * k + 1] * vs));
+      }
+      *vp[c] = make_uint4(h[0], h[1], h[2], h[3]);
+    }
+    // The chunks' largest |v|, as a shallow tree after the stores (it runs
+    // while they complete), kept before the barrier: left to the scheduler it
+    // sinks into the next steps and holds the 16 values in registers there.
+    float t[KB];
+#pragma unroll
+    for (int c = 0; c < KB; ++c) {
+      const float u0 = max3(fabsf(f[c][0]), fabsf(f[c][1]), fabsf(f[c][2]));
+      const float u1 = max3(fabsf(f[c][3]), fabsf(f[c][4]), fabsf(f[c][5]));
+      t[c] = max3(u0, u1, fmaxf(fabsf(f[c][6]), fabsf(f[c][7])));
+    }
+    float tm = t[0];
+#pragma unroll
+    for (int c = 1; c < KB; ++c) tm = fmaxf(tm, t[c]);
+    vmax = fmaxf(vmax, tm);
+    asm volatile("" : "+v"(vmax));
   };
   // Start of iteration i (0 <= i <= nt): wait for group i (K of tile i, V of
   // tile i - 1); for i > 0 convert this lane's chunks of V of tile i - 1 to
@@ -963,6 +1009,37 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
   } else {
     for (int i = 0; i <= nt; ++i) sync(i, true);
   }
+  // The piece's largest |v|: per wavefront by lane swaps, across the
+  // wavefronts through LDS, published by the barrier that ends the tiles.
+  float* const wave_vmax = reinterpret_cast<float*>(lds + kVexpOff);  // [NW]
+  {
+    float x = vmax;
+    x = fmaxf(x, dpp<0xB1>(x));   // lane ^ 1
+    x = fmaxf(x, dpp<0x4E>(x));   // lane ^ 2
+    x = fmaxf(x, dpp<0x141>(x));  // the other quad of each 8
+    x = fmaxf(x, dpp<0x140>(x));  // the other half of each 16
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    if (lane == 0) wave_vmax[w] = x;
+  }
+  __syncthreads();  // all wavefronts are done with the tiles: reuse the LDS
+  {
+    float pm = 0.f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) pm = fmaxf(pm, wave_vmax[k]);
+    const uint32_t pbits = __builtin_amdgcn_readfirstlane(__float_as_uint(pm));  // the same in every lane
+    // E = the exponent of the piece's largest |v| (an all-zero piece fits any ev).
+    const int e_u = pbits == 0u ? ev : min(kEvMax, max(kEvMin, static_cast<int>((pbits >> 23) & 0xffu) - 127));
+    if (!retry && (e_u > ev || (e_u < ev - kEvWindow && ev > kEvMin))) {
+      // Outside the window: the caller runs the piece again with ev = E
+      // (which fits by construction); nothing of this pass is written.
+      ev_carry = e_u;
+      return false;
+    }
+    if (retry) ev_carry = min(kEvMax, ev + 2);  // headroom for the next piece's larger values
+  }
 
   // Row sums: the four lane groups hold different tokens of the same rows.
 #pragma unroll
@@ -970,7 +1047,6 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
     l[rb] += __shfl_xor(l[rb], 16);
     l[rb] += __shfl_xor(l[rb], 32);
   }
-  __syncthreads();  // all wavefronts are done with the tiles: reuse the LDS
   if constexpr (TS == 2) {
     // Merge the two token halves of every slab: half 1 hands its state to half 0.
     float* so = reinterpret_cast<float*>(lds);              // [slab][rb][db][lane][4]
@@ -1008,7 +1084,7 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
 #pragma unroll
     for (int rb = 0; rb < RBR; ++rb) {
       if (!qok[rb]) continue;
-      const float inv = l[rb] > 0.f ? (1.f / kVScale) / l[rb] : 0.f;  // O carries the 2^-8 of V
+      const float inv = l[rb] > 0.f ? exp2i(ev - 15) / l[rb] : 0.f;  // O carries the 2^(15 - ev) of V
       const float lse = l[rb] > 0.f ? (m[rb] + __log2f(l[rb])) * kLn2 : kNegInf;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -1017,6 +1093,7 @@ __device__ __forceinline__ void mfma_piece(const PacParams& p, const TaskInfo& t
       }
     }
   }
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -1292,7 +1369,9 @@ void pac_kernel(PacParams p) {
   const int tid = threadIdx.x;
   if (tb < te && tid < TW) task_lds[tid] = reinterpret_cast<const uint32_t*>(p.tasks + tb)[tid];
   __syncthreads();
-  for (int ti = tb; ti < te; ++ti) {
+  int ev_carry = kEvStart;  // the V scale exponent the next matrix-core piece starts from
+  bool retry = false;  // the task in task_lds runs again with the V scale its first pass found
+  for (int ti = tb; ti < te;) {
     DevTask task;
     __builtin_memcpy(&task, task_lds, sizeof(DevTask));
     uint32_t next_word = 0;
@@ -1325,7 +1404,7 @@ void pac_kernel(PacParams p) {
     const int64_t off = (kvh * p.stride_head + first * p.stride_token) * esz;
     t.kbase = static_cast<const char*>(p.k) + off;
     t.vbase = static_cast<const char*>(p.v) + off;
-    bool done = false;
+    bool done = false, finished = true;
     if constexpr (sizeof(T) == 2) {
       if (t.row_count >= p.mfma_min_rows) {
         // Slabs of 16 RBR rows, TS wavefronts per slab.
@@ -1337,23 +1416,27 @@ void pac_kernel(PacParams p) {
         // are) keeps the default policy.
         if (t.row_count <= 32) {
           if (t.shared)
-            mfma_piece<D, 1, 2, NW, false>(p, t, kvh);
+            finished = mfma_piece<D, 1, 2, NW, false>(p, t, kvh, ev_carry, retry);
           else
-            mfma_piece<D, 1, 2, NW, true>(p, t, kvh);
+            finished = mfma_piece<D, 1, 2, NW, true>(p, t, kvh, ev_carry, retry);
         } else if (t.row_count <= 128) {
           if (t.shared)
-            mfma_piece<D, 2, 2, NW, false>(p, t, kvh);
+            finished = mfma_piece<D, 2, 2, NW, false>(p, t, kvh, ev_carry, retry);
           else
-            mfma_piece<D, 2, 2, NW, true>(p, t, kvh);
+            finished = mfma_piece<D, 2, 2, NW, true>(p, t, kvh, ev_carry, retry);
         } else {
-          mfma_piece<D, 2, 1, NW, false>(p, t, kvh);
+          finished = mfma_piece<D, 2, 1, NW, false>(p, t, kvh, ev_carry, retry);
         }
         done = true;
       }
     }
     if (!done) dot_piece<T, D, NW>(p, t, kvh);
     __syncthreads();  // the piece is finished with the LDS (and with task_lds)
-    if (tid < TW) task_lds[tid] = next_word;
+    retry = !finished;
+    if (finished) {
+      if (tid < TW) task_lds[tid] = next_word;
+      ++ti;
+    }
     __syncthreads();
   }
 }
