@@ -37,7 +37,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed steps first: PAC settles after 30-40 cold steps (about 9 %% faster than the first "
                          "ones on the document-QA tree), which a decode loop reaches within its first milliseconds")
-    ap.add_argument("--config", default="2")
+    ap.add_argument("--config", default="5-mha",
+                    help="workload (default: the largest one that fits one GPU, the skewed MHA tree with ~38 GB "
+                         "of K/V)")
+    ap.add_argument("--no-gate", action="store_true",
+                    help="skip the per-workload PAC + POR measurement of the document-QA, few-shot and "
+                         "speculative trees that follows the main line")
+    ap.add_argument("--gate-warmup", type=int, default=50,
+                    help="untimed cold steps per workload of the gate measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline", action="store_true", help="skip the query-guided comparison")
     ap.add_argument("--no-warm", action="store_true",
@@ -130,12 +137,13 @@ def cpu_baseline(spec, q, k, v, out, budget_s):
     import oracle
 
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
     order = np.random.default_rng(0).permutation(spec.num_queries)
     done, tokens, err = [], 0, 0.0
     t0 = time.perf_counter()
     for r in order:
-        O, _ = oracle.attend(spec, qh, kh, vh, queries=[int(r)])
+        # The oracle gathers each query's path K/V from the device pools
+        # itself (tens of GB never go to the host whole).
+        O, _ = oracle.attend(spec, q, k, v, queries=[int(r)])
         tokens += len(oracle.visible_tokens(spec, int(r)))
         err = max(err, float(abs(out[int(r)].double().cpu().numpy() - O[0]).max()))
         done.append(int(r))
@@ -153,7 +161,8 @@ def cpu_baseline(spec, q, k, v, out, budget_s):
         pass
     return {
         "value": tokens / dt, "unit": "logical KV tokens/s", "cores": threads, "kind": "oracle",
-        "sample": f"{len(done)} of {spec.num_queries} queries (all heads), {tokens} logical tokens, {dt:.1f} s, "
+        "sample": f"{len(done)} of {spec.num_queries} queries (all heads, in a seeded random order), {tokens} "
+                  f"logical tokens, {dt:.1f} s including the gather of each query's path K/V from device memory, "
                   f"float64 numpy on {os.cpu_count()} host CPUs ({model})",
         "parity_max_abs_on_sample": err,
     }
@@ -426,13 +435,7 @@ def main():
                  "estimated_makespan_us": pv["makespan"] / 1e3,
                  "cost_model": "fitted gfx950 table" if plan.cost is not None else "analytic fallback"},
     }
-    traffic = None
-    if os.path.exists(a.traffic):
-        with open(a.traffic) as f:
-            tr = json.load(f)
-        if (tr.get("workload") == spec.name and tr.get("kernel_source_sha") == kernel_sha() and not paged
-                and not a.flatten):
-            traffic = tr.get("hbm_bytes_per_launch")
+    traffic = traffic_for(a.traffic, spec.name) if not paged and not a.flatten else None
     # Algorithmic work of one PAC launch: the unique KV bytes, and 4 d H_q
     # FLOPs per logical (query, token) (QK^T and PV).  The bound is the larger
     # of the two floors; the other is reported beside it.
@@ -452,12 +455,11 @@ def main():
                               secondary={k: other[k] for k in ("bound", "achieved", "peak", "unit", "frac")})
 
     if not a.no_baseline:
-        print("[bench] query-guided baseline", file=sys.stderr, flush=True)
-        bplan = pst.Plan(tree, query_guided=True)
-        bws = pst.workspace(bplan)
-        bpac, bpor, _ = time_steps(torch, pst, bplan, q, kk, vv, out, lse, bws, evict_bufs, max(3, a.steps // 4),
-                                   a.warmup)
-        bms = statistics.mean([x + y for x, y in zip(bpac, bpor)])
+        print("[bench] query-guided baseline (pst_decode_attn_baseline)", file=sys.stderr, flush=True)
+        bws = torch.empty(max(pst.baseline_workspace_bytes(tree, plan.cost), 256), dtype=torch.uint8,
+                          device="cuda")
+        bms = time_baseline(torch, pst, tree, plan.cost, q, kk, vv, out, lse, bws, evict_bufs,
+                            max(3, a.steps // 4), min(a.warmup, 10))
         result["baseline_query_guided"] = {
             "ms_per_step": bms, "speedup_of_tree_path": bms / ms,
             "kv_bytes_read": st["per_query_kv_bytes"],
@@ -471,7 +473,74 @@ def main():
     if not a.no_cpu_baseline:
         print("[bench] oracle on a bounded sample (cpu_baseline)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(spec, q, k, v, out, a.cpu_seconds)
+    if not a.no_gate and not paged and not a.flatten:
+        del q, k, v, kk, vv, out, lse, ws, plan, tree
+        torch.cuda.empty_cache()
+        result["gate"] = gate(torch, pst, workloads, evict_bufs, a)
     print(json.dumps(result), flush=True)
+
+
+def time_baseline(torch, pst, tree, cost, q, k, v, out, lse, ws, evict_bufs, steps, warmup):
+    """Mean cold-cache time of one pst_decode_attn_baseline call (ms)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        evict(pst, evict_bufs)
+        pst.decode_attn_baseline(tree, q, k, v, cost=cost, out=out, lse=lse, ws=ws)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evict(pst, evict_bufs)
+        ev[i][0].record(stream)
+        pst.decode_attn_baseline(tree, q, k, v, cost=cost, out=out, lse=lse, ws=ws)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
+
+
+GATE_CONFIGS = ("2", "3", "4")
+
+
+def gate(torch, pst, workloads, evict_bufs, a):
+    """PAC + POR of the document-QA, few-shot and speculative trees, measured
+    like the main line (cold caches, plan reused), against 8 TB/s on their
+    unique K/V bytes."""
+    rows = {}
+    for name in GATE_CONFIGS:
+        spec = workloads.config(name)
+        print(f"[bench] gate workload {spec.name}", file=sys.stderr, flush=True)
+        q, k, v = workloads.make_tensors(spec, "cuda")
+        tree = pst.Tree.from_spec(spec, out_dtype="f32")
+        plan = pst.Plan(tree)
+        st = workload_stats(spec, tree)
+        out = torch.empty((spec.num_queries, spec.num_q_heads, spec.head_dim), device="cuda", dtype=torch.float32)
+        lse = torch.empty((spec.num_queries, spec.num_q_heads), device="cuda", dtype=torch.float32)
+        ws = pst.workspace(plan)
+        pac, por, _ = time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, a.steps, a.gate_warmup)
+        ms = statistics.mean(x + y for x, y in zip(pac, por))
+        rows[spec.name] = {
+            "config": name, "ms_per_step": ms, "pac_ms": statistics.mean(pac), "por_ms": statistics.mean(por),
+            "unique_kv_bytes": st["unique_kv_bytes"], "logical_tokens": st["logical_tokens"],
+            "logical_tokens_per_s": st["logical_tokens"] / (ms * 1e-3),
+            "unique_kv_GBps": st["unique_kv_bytes"] / (ms * 1e-3) / 1e9,
+            "unique_kv_frac_of_peak": st["unique_kv_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        }
+        del q, k, v, tree, plan, ws, out, lse
+        torch.cuda.empty_cache()
+    return {"warmup": a.gate_warmup, "steps": a.steps, "workloads": rows}
+
+
+def traffic_for(path, workload):
+    """HBM bytes per PAC launch for this workload from the counter summary,
+    if it was taken on the current kernel code (else None)."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    entries = tr.get("entries", [tr])
+    sha = kernel_sha()
+    for e in entries:
+        if e.get("workload") == workload and e.get("kernel_source_sha") == sha:
+            return e.get("hbm_bytes_per_launch")
+    return None
 
 
 def kernel_sha():

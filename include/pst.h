@@ -152,9 +152,19 @@ pst_status pst_tree_build(const pst_tree_desc* desc, const pst_shape* shape, uin
 
 /* Decode-step growth: new lengths for every node, each >= the current one
  * (masked nodes stay <= 64).  Plans made from this tree stay valid: a node's
- * last piece simply grows.  Uploads the lengths on `stream`.
- * PST_E_UNSUPPORTED (nothing changed) while a flattened plan of the tree
- * is live. */
+ * last piece simply grows (CoDec, implementation section: the partition is
+ * reused across decoding steps).  The new lengths and the plans' patched
+ * pieces are copied to the device on `stream` from pinned staging buffers
+ * that the tree keeps (four, used in turn): the call queues the copies and
+ * returns without waiting for them, except that it waits for the copies it
+ * queued four calls earlier before writing their buffer again.  Launches
+ * queued on `stream` after the call see the new lengths; work on another
+ * stream must be ordered after `stream` by the caller, and a plan must not
+ * be freed before the copies queued into it have run (synchronise `stream`).
+ * Argument and tree checks come first: PST_E_INVALID_ARG / PST_E_INVALID_TREE
+ * and PST_E_UNSUPPORTED (a flattened plan of the tree is live) change
+ * nothing, nor does PST_E_OOM (the first call, or a call after plans were
+ * added, allocates the staging memory). */
 pst_status pst_tree_set_lengths(pst_tree_t tree, const int32_t* kv_len, void* stream);
 
 /* Host views of the index, valid until the tree is freed. */
@@ -187,6 +197,16 @@ pst_status pst_tree_get_index(pst_tree_t tree, pst_index_view* view);
 pst_status pst_cost_model_create(int32_t n_rows, const int32_t* rows_grid, int32_t n_len,
                                  const int32_t* len_grid, const int64_t* table, pst_cost_model_t* out);
 pst_status pst_cost_model_lookup(pst_cost_model_t cost, int32_t rows, int64_t len, int64_t* ns);
+
+/* The same model read from a JSON file (the format of the fitted gfx950
+ * tables the library ships): an object whose "rows_grid" and "len_grid" are
+ * arrays of integers and whose "table_ns" is an array holding one array of
+ * integer nanoseconds per rows_grid point, each with one entry per len_grid
+ * point; other keys are ignored.  The values must satisfy the rules of
+ * pst_cost_model_create.  PST_E_INVALID_ARG (message names the file and the
+ * problem) when the file cannot be read, is not such a JSON object, or holds
+ * an invalid table; *out is then NULL. */
+pst_status pst_cost_model_load(const char* json_path, pst_cost_model_t* out);
 
 /* pst_plan options (zero-initialise for defaults) */
 #define PST_PLAN_QUERY_GUIDED 1u /* FlashDecoding-style baseline: one query per row group (shared KV re-read per query) */
@@ -310,7 +330,23 @@ pst_status pst_pac(pst_plan_t plan, const void* q, const void* k_pool, const voi
 pst_status pst_por(pst_plan_t plan, void* out, float* lse_out, const void* workspace,
                    size_t workspace_bytes, void* stream);
 
-/* Release a tree, plan or cost model.  NULL is accepted. */
+/* The FlashDecoding-style comparator in the same library (KV-cache blog
+ * section 4, FlashDecoding; DEFT section 3.3, Q-guided grouping): every
+ * query's g rows form their own row groups, so a node shared by n_q queries
+ * is read n_q times instead of once; the pieces, kernels and merge are those
+ * of pst_decode_attn.  The tree keeps the query-guided plan it needs (made on
+ * the first call with this cost model, NULL = the built-in model, default bins
+ * for the current device; remade when the cost model changes) and frees it
+ * with itself; growth through pst_tree_set_lengths keeps it valid.  The
+ * tensors, their layouts and the workspace rules are those of
+ * pst_decode_attn; the workspace size is pst_baseline_workspace_size's. */
+pst_status pst_baseline_workspace_size(pst_tree_t tree, pst_cost_model_t cost, void* stream, size_t* bytes);
+pst_status pst_decode_attn_baseline(pst_tree_t tree, pst_cost_model_t cost, const void* q, const void* k_pool,
+                                    const void* v_pool, void* out, float* lse_out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* Release a tree, plan or cost model.  NULL is accepted.  A tree with live
+ * plans (from pst_plan) is refused: free its plans first. */
 pst_status pst_free(void* obj);
 
 /* Thread-local message of the last failure in this thread ("" if none). */

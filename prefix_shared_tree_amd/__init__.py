@@ -17,7 +17,6 @@ the library as raw pointers, kernels run on torch's current stream.
 from __future__ import annotations
 
 import ctypes as C
-import json
 import os
 from typing import Optional
 
@@ -56,7 +55,7 @@ EXPORTS = [
     "pst_tree_build", "pst_tree_set_lengths", "pst_tree_get_index", "pst_cost_model_create",
     "pst_cost_model_lookup", "pst_plan", "pst_plan_workspace_size", "pst_plan_get", "pst_decode_attn",
     "pst_pac", "pst_por", "pst_free", "pst_last_error", "pst_device_info", "pst_bench_flush",
-    "pst_bench_read",
+    "pst_bench_read", "pst_cost_model_load", "pst_baseline_workspace_size", "pst_decode_attn_baseline",
 ]
 
 
@@ -121,6 +120,9 @@ _sig = {
     "pst_device_info": [C.POINTER(C.c_int32), C.POINTER(C.c_int32)],
     "pst_bench_flush": [_P, C.c_size_t, _P],
     "pst_bench_read": [_P, C.c_size_t, _P, _P],
+    "pst_cost_model_load": [C.c_char_p, C.POINTER(_P)],
+    "pst_baseline_workspace_size": [_P, _P, _P, C.POINTER(C.c_size_t)],
+    "pst_decode_attn_baseline": [_P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P],
 }
 for _name, _args in _sig.items():
     _f = getattr(_lib, _name)
@@ -264,6 +266,8 @@ class Tree:
 
     def set_lengths(self, kv_len, stream=None):
         kv_len, p = _arr(kv_len, np.int32)
+        if kv_len.shape != (self.num_nodes,):
+            raise ValueError(f"kv_len needs one length per node ({self.num_nodes}), got shape {kv_len.shape}")
         _check(_lib.pst_tree_set_lengths(self._h, p, _stream(stream) if not self.host_only else C.c_void_p(0)))
 
     def free(self):
@@ -288,13 +292,16 @@ class CostModel:
         lg, p_lg = _arr(len_grid, np.int32)
         tb, p_tb = _arr(np.asarray(table).reshape(len(rg), len(lg)), np.int64)
         _check(_lib.pst_cost_model_create(len(rg), p_rg, len(lg), p_lg, p_tb, C.byref(self._h)))
-        self.rows_grid, self.len_grid, self.table = rg, lg, tb
+        self.path = None
 
     @classmethod
     def load(cls, path):
-        with open(path) as f:
-            d = json.load(f)
-        return cls(d["rows_grid"], d["len_grid"], d["table_ns"])
+        """A fitted table from its JSON file (``pst_cost_model_load``)."""
+        self = cls.__new__(cls)
+        self._h = C.c_void_p()
+        _check(_lib.pst_cost_model_load(os.fsencode(path), C.byref(self._h)))
+        self.path = path
+        return self
 
     def lookup(self, rows: int, length: int) -> int:
         out = C.c_int64()
@@ -390,29 +397,23 @@ class Plan:
             pass
 
 
-def _check_tensors(tree, q, k_pool, v_pool, out, lse):
-    """Sizes, dtypes and devices against the tree's shape: the C ABI only sees pointers."""
-    import torch
+def _check_one(name, t, dt):
+    if t.dtype != dt:
+        raise ValueError(f"{name} must be {dt}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name} must be 16-byte aligned")
 
-    idt = torch.float32 if tree.in_dtype == PST_F32 else torch.bfloat16
-    odt = torch.float32 if tree.out_dtype == PST_F32 else torch.bfloat16
-    B, hq, d = tree.num_queries, tree.num_q_heads, tree.head_dim
-    for name, t, dt in (("q", q, idt), ("k_pool", k_pool, idt), ("v_pool", v_pool, idt), ("out", out, odt)):
-        if t.dtype != dt:
-            raise ValueError(f"{name} must be {dt}, got {t.dtype}")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-        if t.device.type != "cuda":
-            raise ValueError(f"{name} must be on the GPU")
-        if t.data_ptr() % 16:
-            raise ValueError(f"{name} must be 16-byte aligned")
-    if q.numel() < B * hq * d or out.numel() < B * hq * d:
-        raise ValueError("q / out smaller than [num_queries, num_q_heads, head_dim]")
-    need = tree.kv_extent
-    if k_pool.numel() < need or v_pool.numel() < need:
-        raise ValueError(f"K/V pools hold fewer than the {need} elements the tree's layout addresses")
-    if lse is not None and (lse.dtype != torch.float32 or lse.numel() < B * hq or not lse.is_contiguous()):
-        raise ValueError("lse must be contiguous float32 with num_queries * num_q_heads elements")
+
+def _check_tensors(tree, q, k_pool, v_pool, out, lse):
+    """Sizes, dtypes and devices against the tree's shape: the C ABI only sees
+    pointers, and the kernels size their reads from the plan, not from the
+    tensors."""
+    _check_inputs(tree, q, k_pool, v_pool)
+    _check_outputs(tree, out, lse)
 
 
 def _ptr(t):
@@ -444,12 +445,78 @@ def decode_attn(plan: Plan, q, k_pool, v_pool, *, out=None, lse=None, want_lse=T
     return out, lse
 
 
+def decode_attn_baseline(tree: Tree, q, k_pool, v_pool, *, cost=None, out=None, lse=None, want_lse=True, ws=None,
+                         stream=None):
+    """``pst_decode_attn_baseline`` (the FlashDecoding-style comparator: shared
+    nodes read once per query): returns (out, lse) like :func:`decode_attn`.
+    ``cost`` None selects the fitted table shipped for the tree's head layout."""
+    import torch
+
+    if cost is None:
+        cost = default_cost_model(tree.head_dim, tree.num_q_heads, tree.num_kv_heads, tree.in_dtype)
+    ch = cost._h if cost is not None else None
+    if out is None:
+        odt = torch.float32 if tree.out_dtype == PST_F32 else torch.bfloat16
+        out = torch.empty((tree.num_queries, tree.num_q_heads, tree.head_dim), dtype=odt, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((tree.num_queries, tree.num_q_heads), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(max(baseline_workspace_bytes(tree, cost, stream), 256), dtype=torch.uint8, device=q.device)
+    _check_tensors(tree, q, k_pool, v_pool, out, lse)
+    _check(_lib.pst_decode_attn_baseline(tree._h, ch, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse),
+                                         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out, lse
+
+
+def baseline_workspace_bytes(tree: Tree, cost=None, stream=None) -> int:
+    """``pst_baseline_workspace_size`` (makes the tree's query-guided plan if needed)."""
+    n = C.c_size_t()
+    _check(_lib.pst_baseline_workspace_size(tree._h, cost._h if cost is not None else None, _stream(stream),
+                                            C.byref(n)))
+    return n.value
+
+
+def _check_inputs(tree, q, k_pool, v_pool):
+    """q and the K/V pools against the tree's shape (see :func:`_check_tensors`)."""
+    import torch
+
+    idt = torch.float32 if tree.in_dtype == PST_F32 else torch.bfloat16
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _check_one(name, t, idt)
+    if q.numel() < tree.num_queries * tree.num_q_heads * tree.head_dim:
+        raise ValueError("q smaller than [num_queries, num_q_heads, head_dim]")
+    need = tree.kv_extent
+    if k_pool.numel() < need or v_pool.numel() < need:
+        raise ValueError(f"K/V pools hold fewer than the {need} elements the tree's layout addresses")
+
+
+def _check_outputs(tree, out, lse):
+    import torch
+
+    odt = torch.float32 if tree.out_dtype == PST_F32 else torch.bfloat16
+    _check_one("out", out, odt)
+    if out.numel() < tree.num_queries * tree.num_q_heads * tree.head_dim:
+        raise ValueError("out smaller than [num_queries, num_q_heads, head_dim]")
+    if lse is not None and (lse.dtype != torch.float32 or lse.numel() < tree.num_queries * tree.num_q_heads
+                            or not lse.is_contiguous() or lse.device.type != "cuda"):
+        raise ValueError("lse must be a contiguous float32 GPU tensor with num_queries * num_q_heads elements")
+
+
+def _check_ws(plan, ws):
+    if ws is None or ws.device.type != "cuda" or ws.numel() * ws.element_size() < plan.workspace_bytes:
+        raise ValueError(f"the workspace must be a GPU tensor of at least {plan.workspace_bytes} bytes")
+
+
 def pac(plan: Plan, q, k_pool, v_pool, ws, stream=None):
+    _check_inputs(plan.tree, q, k_pool, v_pool)
+    _check_ws(plan, ws)
     _check(_lib.pst_pac(plan._h, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(ws), ws.numel() * ws.element_size(),
                         _stream(stream)))
 
 
 def por(plan: Plan, out, lse, ws, stream=None):
+    _check_outputs(plan.tree, out, lse)
+    _check_ws(plan, ws)
     _check(_lib.pst_por(plan._h, _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 

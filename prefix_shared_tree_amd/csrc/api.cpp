@@ -99,8 +99,21 @@ struct pst_tree_s {
   bool on_device = false;
   int device = -1;
   uint64_t generation = 0;  // bumped when the device index is rebuilt
-  int live_plans = 0;
-  std::vector<pst_plan_s*> plans;  // live plans: their device tasks follow length changes
+  int live_plans = 0;               // plans handed out by pst_plan and not yet freed
+  std::vector<pst_plan_s*> plans;  // every plan of this tree: their device tasks follow length changes
+  pst_plan_s* baseline = nullptr;  // query-guided plan of pst_decode_attn_baseline (owned by the tree)
+  // Pinned staging buffers of pst_tree_set_lengths, used in turn: a copy from
+  // pinned memory runs asynchronously, and a buffer is written again only
+  // after the copy queued from it kLengthSlots calls earlier has finished.
+  static constexpr int kLengthSlots = 4;
+  struct Staging {
+    char* host = nullptr;  // hipHostMalloc
+    size_t bytes = 0;
+    hipEvent_t copied = nullptr;  // recorded after the copies out of `host`
+  };
+  Staging staging[kLengthSlots];
+  int staging_next = 0;
+  uint64_t baseline_cost = 0;      // id of the cost model it was made with (0 = built-in model)
   void* d_arena = nullptr;  // holds every d_ array below
   int64_t* d_node_off = nullptr;
   int32_t* d_node_len = nullptr;
@@ -133,10 +146,19 @@ struct pst_plan_s {
 
 struct pst_cost_s {
   uint32_t magic = kCostMagic;
+  uint64_t id = 0;  // unique per model made in this process
   CostModel model;
 };
 
 static void free_tree_device(pst_tree_s* t) {
+  for (auto& st : t->staging) {
+    if (st.copied) {
+      (void)hipEventSynchronize(st.copied);
+      (void)hipEventDestroy(st.copied);
+    }
+    if (st.host) (void)hipHostFree(st.host);
+    st = pst_tree_s::Staging{};
+  }
   if (t->d_arena) (void)hipFree(t->d_arena);
   t->d_arena = nullptr;
   t->d_node_off = nullptr;
@@ -157,6 +179,18 @@ static void free_plan_device(pst_plan_s* p) {
   p->d_flat_query = p->d_flat_rows = nullptr;
   p->d_flat_mask = nullptr;
   p->on_device = false;
+}
+
+// Unlinks a plan from its tree's list and frees it (the caller fixes the
+// tree's count of handed-out plans).
+static void release_plan(pst_plan_s* p) {
+  if (p->tree) {
+    auto& v = p->tree->plans;
+    v.erase(std::remove(v.begin(), v.end(), p), v.end());
+  }
+  free_plan_device(p);
+  p->magic = 0;
+  delete p;
 }
 
 static int elem_bytes(int dt) { return dt == PST_F32 ? 4 : 2; }
@@ -226,9 +260,10 @@ pst_status pst_tree_build(const pst_tree_desc* desc, const pst_shape* shape, uin
   }
   t->pool_tokens = shape->pool_tokens > 0 ? shape->pool_tokens : need;
   if (need > t->pool_tokens) {
+    const bool paged = t->ix.page_size > 0;
     delete t;
-    set_error(t->ix.page_size > 0 ? "a page lies outside the K/V pools (pool_tokens too small)"
-                                  : "a node lies outside the K/V pools (pool_tokens too small)");
+    set_error(paged ? "a page lies outside the K/V pools (pool_tokens too small)"
+                    : "a node lies outside the K/V pools (pool_tokens too small)");
     return PST_E_INVALID_TREE;
   }
   if (t->shape.kv_stride_token == 0) t->shape.kv_stride_token = shape->head_dim;
@@ -309,6 +344,42 @@ pst_status pst_tree_set_lengths(pst_tree_t t, const int32_t* kv_len, void* strea
       return PST_E_INVALID_TREE;
     }
   }
+  // The device copies of the new lengths and of every plan's tasks leave from
+  // a pinned staging buffer (so the copies are asynchronous: no host wait).
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  size_t need = 0;
+  pst_tree_s::Staging* slot = nullptr;
+  if (t->on_device && ix.N > 0) {
+    need = align(ix.N * sizeof(int32_t));
+    for (const pst_plan_s* p : t->plans)
+      if (p->on_device) need += align(p->dev_tasks.size() * sizeof(DevTask));
+    slot = &t->staging[t->staging_next];
+    if (slot->copied) {
+      hipError_t e = hipEventSynchronize(slot->copied);  // the copies queued from it kLengthSlots calls ago
+      if (e != hipSuccess) return hip_fail("hipEventSynchronize", e);
+    } else {
+      hipError_t e = hipEventCreateWithFlags(&slot->copied, hipEventDisableTiming);
+      if (e != hipSuccess) {
+        slot->copied = nullptr;
+        return hip_fail("hipEventCreateWithFlags", e);
+      }
+    }
+    if (slot->bytes < need) {
+      if (slot->host) (void)hipHostFree(slot->host);
+      slot->host = nullptr;
+      slot->bytes = 0;
+      void* h = nullptr;
+      hipError_t e = hipHostMalloc(&h, need, hipHostMallocDefault);
+      if (e != hipSuccess) {
+        (void)hipGetLastError();
+        set_error(std::string("hipHostMalloc failed: ") + hipGetErrorString(e));
+        return PST_E_OOM;
+      }
+      slot->host = static_cast<char*>(h);
+      slot->bytes = need;
+    }
+  }
   // Visible counts: every node on a path grows, except that a query's own
   // masked node keeps its mask bits.
   for (int32_t r = 0; r < ix.B; ++r) {
@@ -324,11 +395,6 @@ pst_status pst_tree_set_lengths(pst_tree_t t, const int32_t* kv_len, void* strea
     ix.visible[r] = vis;
   }
   std::copy(kv_len, kv_len + ix.N, ix.kv_len.begin());
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (t->on_device && ix.N > 0) {
-    hipError_t e = hipMemcpyAsync(t->d_node_len, ix.kv_len.data(), ix.N * sizeof(int32_t), hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return hip_fail("hipMemcpyAsync", e);
-  }
   // The last piece of every node absorbs the growth: patch the plans' tasks.
   for (pst_plan_s* p : t->plans) {
     for (size_t i = 0; i < p->r.tasks.size(); ++i) {
@@ -337,15 +403,25 @@ pst_status pst_tree_set_lengths(pst_tree_t t, const int32_t* kv_len, void* strea
       const int32_t len = ix.kv_len[a.node] - a.kv_begin;
       if (i < p->dev_tasks.size()) p->dev_tasks[i].kv_len = len;
     }
-    if (p->on_device && !p->dev_tasks.empty()) {
-      hipError_t e = hipMemcpyAsync(p->d_tasks, p->dev_tasks.data(), p->dev_tasks.size() * sizeof(DevTask),
-                                    hipMemcpyHostToDevice, s);
-      if (e != hipSuccess) return hip_fail("hipMemcpyAsync", e);
-    }
   }
-  if (t->on_device) {
-    hipError_t e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return hip_fail("hipStreamSynchronize", e);
+  if (slot) {
+    size_t off = 0;
+    std::memcpy(slot->host, ix.kv_len.data(), ix.N * sizeof(int32_t));
+    hipError_t e = hipMemcpyAsync(t->d_node_len, slot->host, ix.N * sizeof(int32_t), hipMemcpyHostToDevice, s);
+    off += align(ix.N * sizeof(int32_t));
+    for (pst_plan_s* p : t->plans) {
+      if (e != hipSuccess) break;
+      if (!p->on_device) continue;
+      const size_t bytes = p->dev_tasks.size() * sizeof(DevTask);
+      if (bytes) {
+        std::memcpy(slot->host + off, p->dev_tasks.data(), bytes);
+        e = hipMemcpyAsync(p->d_tasks, slot->host + off, bytes, hipMemcpyHostToDevice, s);
+      }
+      off += align(bytes);
+    }
+    if (e == hipSuccess) e = hipEventRecord(slot->copied, s);
+    t->staging_next = (t->staging_next + 1) % pst_tree_s::kLengthSlots;
+    if (e != hipSuccess) return hip_fail("length upload", e);
   }
   return PST_OK;
 }
@@ -373,13 +449,8 @@ pst_status pst_tree_get_index(pst_tree_t t, pst_index_view* v) {
   return PST_OK;
 }
 
-pst_status pst_cost_model_create(int32_t n_rows, const int32_t* rows_grid, int32_t n_len, const int32_t* len_grid,
-                                 const int64_t* table, pst_cost_model_t* out) {
-  if (!out) {
-    set_error("out is NULL");
-    return PST_E_INVALID_ARG;
-  }
-  *out = nullptr;
+static pst_status make_cost(int32_t n_rows, const int32_t* rows_grid, int32_t n_len, const int32_t* len_grid,
+                            const int64_t* table, pst_cost_model_t* out) {
   if (n_rows < 1 || n_len < 2 || !rows_grid || !len_grid || !table) {
     set_error("cost table needs >= 1 rows point, >= 2 length points and non-NULL arrays");
     return PST_E_INVALID_ARG;
@@ -407,11 +478,47 @@ pst_status pst_cost_model_create(int32_t n_rows, const int32_t* rows_grid, int32
     set_error("host allocation failed");
     return PST_E_OOM;
   }
+  static uint64_t next_id = 0;
+  c->id = ++next_id;
   c->model.rows_grid.assign(rows_grid, rows_grid + n_rows);
   c->model.len_grid.assign(len_grid, len_grid + n_len);
   c->model.table.assign(table, table + static_cast<size_t>(n_rows) * n_len);
   *out = c;
   return PST_OK;
+}
+
+pst_status pst_cost_model_create(int32_t n_rows, const int32_t* rows_grid, int32_t n_len, const int32_t* len_grid,
+                                 const int64_t* table, pst_cost_model_t* out) {
+  if (!out) {
+    set_error("out is NULL");
+    return PST_E_INVALID_ARG;
+  }
+  *out = nullptr;
+  return make_cost(n_rows, rows_grid, n_len, len_grid, table, out);
+}
+
+pst_status pst_cost_model_load(const char* json_path, pst_cost_model_t* out) {
+  if (!out) {
+    set_error("out is NULL");
+    return PST_E_INVALID_ARG;
+  }
+  *out = nullptr;
+  if (!json_path) {
+    set_error("json_path is NULL");
+    return PST_E_INVALID_ARG;
+  }
+  std::vector<int32_t> rows, lens;
+  std::vector<int64_t> table;
+  pst_status st = load_cost_json(json_path, &rows, &lens, &table);
+  if (st != PST_OK) return st;
+  if (rows.size() > INT32_MAX || lens.size() > INT32_MAX) {
+    set_error("cost table too large");
+    return PST_E_INVALID_ARG;
+  }
+  st = make_cost(static_cast<int32_t>(rows.size()), rows.data(), static_cast<int32_t>(lens.size()), lens.data(),
+                 table.data(), out);
+  if (st != PST_OK) set_error(std::string("cost table ") + json_path + ": " + g_last_error);
+  return st;
 }
 
 pst_status pst_cost_model_lookup(pst_cost_model_t c, int32_t rows, int64_t len, int64_t* ns) {
@@ -441,11 +548,10 @@ pst_status pst_device_info(int32_t* num_cu, int32_t* per_cu) {
   return PST_OK;
 }
 
-pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* opts, void* stream, pst_plan_t* out) {
-  if (!out) {
-    set_error("out is NULL");
-    return PST_E_INVALID_ARG;
-  }
+// Builds a plan object (host arrays, and the device copy unless host-only)
+// without registering it with its tree.
+static pst_status make_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* opts, void* stream,
+                            pst_plan_t* out) {
   *out = nullptr;
   if (!t || t->magic != kTreeMagic) {
     set_error("bad tree");
@@ -608,9 +714,19 @@ pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* op
     }
     p->on_device = true;
   }
-  t->live_plans++;
-  t->plans.push_back(p);
   *out = p;
+  return PST_OK;
+}
+
+pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* opts, void* stream, pst_plan_t* out) {
+  if (!out) {
+    set_error("out is NULL");
+    return PST_E_INVALID_ARG;
+  }
+  pst_status st = make_plan(t, cost, opts, stream, out);
+  if (st != PST_OK) return st;
+  t->live_plans++;
+  t->plans.push_back(*out);
   return PST_OK;
 }
 
@@ -778,6 +894,63 @@ pst_status pst_decode_attn(pst_plan_t p, const void* q, const void* k, const voi
   return pst_por(p, out, lse_out, ws, ws_bytes, stream);
 }
 
+// The tree's query-guided plan under `cost` (made on first use, and again
+// when the cost model or the tree's generation changed).
+static pst_status baseline_plan(pst_tree_t t, pst_cost_model_t cost, void* stream, pst_plan_s** out) {
+  *out = nullptr;
+  if (!t || t->magic != kTreeMagic) {
+    set_error("bad tree");
+    return PST_E_INVALID_ARG;
+  }
+  if (cost && cost->magic != kCostMagic) {
+    set_error("bad cost model");
+    return PST_E_INVALID_ARG;
+  }
+  if (!t->on_device) {
+    set_error("tree was built host-only");
+    return PST_E_NO_DEVICE;
+  }
+  const uint64_t cid = cost ? cost->id : 0;
+  if (t->baseline && (t->baseline_cost != cid || t->baseline->generation != t->generation)) {
+    release_plan(t->baseline);
+    t->baseline = nullptr;
+  }
+  if (!t->baseline) {
+    pst_plan_opts o{};
+    o.flags = PST_PLAN_QUERY_GUIDED;
+    pst_plan_s* p = nullptr;
+    pst_status st = make_plan(t, cost, &o, stream, &p);
+    if (st != PST_OK) return st;
+    t->plans.push_back(p);  // follows length changes like any plan of the tree
+    t->baseline = p;
+    t->baseline_cost = cid;
+  }
+  *out = t->baseline;
+  return PST_OK;
+}
+
+pst_status pst_baseline_workspace_size(pst_tree_t t, pst_cost_model_t cost, void* stream, size_t* bytes) {
+  if (!bytes) {
+    set_error("bytes is NULL");
+    return PST_E_INVALID_ARG;
+  }
+  pst_plan_s* p = nullptr;
+  pst_status st = baseline_plan(t, cost, stream, &p);
+  if (st != PST_OK) return st;
+  size_t ob = 0;
+  workspace_layout(p, &ob, bytes);
+  return PST_OK;
+}
+
+pst_status pst_decode_attn_baseline(pst_tree_t t, pst_cost_model_t cost, const void* q, const void* k,
+                                    const void* v, void* out, float* lse_out, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  pst_plan_s* p = nullptr;
+  pst_status st = baseline_plan(t, cost, stream, &p);
+  if (st != PST_OK) return st;
+  return pst_decode_attn(p, q, k, v, out, lse_out, ws, ws_bytes, stream);
+}
+
 pst_status pst_free(void* obj) {
   if (!obj) return PST_OK;
   const uint32_t magic = *static_cast<uint32_t*>(obj);
@@ -787,6 +960,8 @@ pst_status pst_free(void* obj) {
       set_error("tree still has live plans: free them first");
       return PST_E_INVALID_ARG;
     }
+    if (t->baseline) release_plan(t->baseline);
+    t->baseline = nullptr;
     free_tree_device(t);
     t->magic = 0;
     delete t;
@@ -794,14 +969,12 @@ pst_status pst_free(void* obj) {
   }
   if (magic == kPlanMagic) {
     pst_plan_s* p = static_cast<pst_plan_s*>(obj);
-    if (p->tree) {
-      p->tree->live_plans--;
-      auto& v = p->tree->plans;
-      v.erase(std::remove(v.begin(), v.end(), p), v.end());
+    if (p->tree && p == p->tree->baseline) {
+      set_error("this plan belongs to its tree (pst_decode_attn_baseline); it goes with the tree");
+      return PST_E_INVALID_ARG;
     }
-    free_plan_device(p);
-    p->magic = 0;
-    delete p;
+    if (p->tree) p->tree->live_plans--;
+    release_plan(p);
     return PST_OK;
   }
   if (magic == kCostMagic) {

@@ -110,6 +110,11 @@ pst_status build_plan(const TreeIndex& ix, int32_t g, const CostModel& cost, con
 pst_status build_flat_plan(const TreeIndex& ix, int32_t g, const CostModel& cost, const PlanOptions& o,
                            PlanResult* out);
 CostModel analytic_cost_model(int32_t g, int32_t head_dim, int32_t elem_bytes);
+// Reads a profiled table (keys rows_grid, len_grid, table_ns) from a JSON
+// file; the table comes back row-major.  Validation of its values is the
+// caller's.
+pst_status load_cost_json(const char* path, std::vector<int32_t>* rows_grid, std::vector<int32_t>* len_grid,
+                          std::vector<int64_t>* table);
 
 // ---------------------------------------------------------------------------
 // Kernel parameter blocks (passed by value)

@@ -89,6 +89,12 @@ class DecodeSession:
         self.v[:, ok] = v[:, src[ok]]
         self.plan_kw = dict(plan_kw or {})
         self.host_only = bool(host_only)
+        # Pinned staging for each step's new pool rows, used in turn (a copy
+        # from pinned memory does not wait for the device); a buffer is
+        # refilled once the copy queued from it has run.
+        self._rows_pinned = []
+        self._rows_done = []
+        self._rows_next = 0
         self.replan_every = int(replan_every)
         self.steps = 0
         self.steps_since_plan = 0
@@ -153,16 +159,41 @@ class DecodeSession:
         return pages * P + positions % P
 
     # -- steps ---------------------------------------------------------------
-    def append(self, k_new, v_new):
-        """Append one token per query: ``k_new``, ``v_new`` are [B, H_kv, d]."""
+    def _device_rows(self, rows):
+        """``rows`` (int64 numpy) on the pool's device, copied from pinned
+        memory without a host wait when the pool is on a GPU."""
         import torch
 
+        if self.k.device.type != "cuda":
+            return torch.from_numpy(rows)
+        slots = 4
+        if not self._rows_pinned:
+            self._rows_pinned = [None] * slots
+            self._rows_done = [None] * slots
+        i = self._rows_next
+        self._rows_next = (i + 1) % slots
+        if self._rows_done[i] is not None:
+            self._rows_done[i].synchronize()  # the copy queued from this buffer `slots` steps ago
+        if self._rows_pinned[i] is None or self._rows_pinned[i].numel() < len(rows):
+            self._rows_pinned[i] = torch.empty(max(len(rows), 64), dtype=torch.int64, pin_memory=True)
+        buf = self._rows_pinned[i][:len(rows)]
+        buf.numpy()[:] = rows
+        out = buf.to(self.k.device, non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self._rows_done[i] = ev
+        return out
+
+    def append(self, k_new, v_new):
+        """Append one token per query: ``k_new``, ``v_new`` are [B, H_kv, d].
+        Nothing here waits for the device: the new rows' pool positions and
+        the new lengths travel from pinned memory."""
         qn = self.query_node.astype(np.int64)
         pos = self.kv_len[qn].astype(np.int64)
         cap = np.asarray([len(self.pages[i]) for i in qn], dtype=np.int64) * self.page_size
         if (pos + 1 > cap).any():
             raise ValueError("a leaf has used its spare capacity (max_new_tokens)")
-        rows = torch.from_numpy(self.pool_rows(qn, pos)).to(self.k.device)
+        rows = self._device_rows(self.pool_rows(qn, pos))
         self.k[:, rows] = k_new.transpose(0, 1).to(self.k.dtype)
         self.v[:, rows] = v_new.transpose(0, 1).to(self.v.dtype)
         self.kv_len[qn] += 1

@@ -41,19 +41,82 @@ def run(spec, *, out_dtype="f32", q_scale=1.0, tensors=None, **plan_kw):
     return (q, k, v), plan, out, lse
 
 
-def check(spec, tensors, out, lse, queries=None, tol=None):
+def check(spec, tensors, out, lse, queries=None, tol=None, lse_tol=None, by_node=False):
+    """Max-abs errors of ``out`` and ``lse`` on ``queries`` against the oracle.
+
+    ``by_node``: at full size, the oracle's answer is formed per path node
+    (see :func:`oracle_by_node`) instead of per query."""
     q, k, v = tensors
     if queries is None:
         queries = list(range(spec.num_queries))
-    O, L = oracle.attend(spec, q, k, v, queries=queries)
+    if by_node:
+        O, L = oracle_by_node(spec, q, k, v, queries)
+    else:
+        O, L = oracle.attend(spec, q, k, v, queries=queries)
     got = out[queries].double().cpu().numpy()
     tol = TOL[spec.dtype] if tol is None else tol
+    lse_tol = max(tol, 1e-5) * 4 if lse_tol is None else lse_tol
     err = np.abs(got - O).max() if len(queries) else 0.0
     lerr = np.abs(lse[queries].double().cpu().numpy() - L).max() if len(queries) else 0.0
     say(f"  {spec.name}: max|dO| = {err:.3e}, max|dLSE| = {lerr:.3e} over {len(queries)} queries")
     assert err <= tol, err
-    assert lerr <= max(tol, 1e-5) * 4, lerr
+    assert lerr <= lse_tol, lerr
     return err
+
+
+def oracle_by_node(spec, q, k, v, queries):
+    """The oracle for ``queries`` of an unmasked tree whose K/V are too large
+    to gather once per query: each node on the queries' paths is copied from
+    the device once, every checked query's partial attention over it comes
+    from ``oracle.partial_attend`` in float64, and each query's partials are
+    merged with ``oracle.lse_merge`` (the split-and-merge identity the CPU
+    tests pin against one full softmax to 1e-12)."""
+    assert spec.node_masked is None or not np.asarray(spec.node_masked).any()
+    hq, hkv, d = spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    g = hq // hkv
+    scale = 1.0 / math.sqrt(d)
+    paths = []
+    for r in queries:
+        path, n = [], int(spec.query_node[r])
+        while n >= 0:
+            path.append(n)
+            n = int(spec.parent[n])
+        paths.append(path[::-1])
+    through = {}
+    for qi, path in enumerate(paths):
+        for n in path:
+            through.setdefault(n, []).append(qi)
+    qh = q[queries].cpu().double().numpy()  # [n, hq, d]
+    parts = [dict() for _ in queries]  # node -> (O [hq, d], LSE [hq])
+    for n in sorted(through):
+        rs = through[n]
+        a, L = int(spec.kv_offset[n]), int(spec.kv_len[n])
+        O = np.zeros((len(rs), hq, d))
+        lse = np.zeros((len(rs), hq))
+        for kh in range(hkv):
+            K = k[kh, a:a + L].cpu().double().numpy()
+            V = v[kh, a:a + L].cpu().double().numpy()
+            heads = slice(kh * g, (kh + 1) * g)
+            rows = qh[rs][:, heads].reshape(-1, d)
+            Oh, _, _, lh = oracle.partial_attend(rows, K, V, scale)
+            O[:, heads] = Oh.reshape(len(rs), g, d)
+            lse[:, heads] = lh.reshape(len(rs), g)
+        for j, qi in enumerate(rs):
+            parts[qi][n] = (O[j], lse[j])
+    Oall = np.zeros((len(queries), hq, d))
+    Lall = np.zeros((len(queries), hq))
+    for qi, path in enumerate(paths):
+        Oall[qi], Lall[qi] = oracle.lse_merge([parts[qi][n][0] for n in path], [parts[qi][n][1] for n in path])
+    return Oall, Lall
+
+
+def per_leaf_queries(spec):
+    """One query (the lowest id) per node some query sits on: every node of
+    the tree, and so every piece of every node, lies on a checked path."""
+    first = {}
+    for r, n in enumerate(spec.query_node):
+        first.setdefault(int(n), r)
+    return sorted(first.values())
 
 
 def sample(n, k, seed=0):
@@ -71,35 +134,53 @@ def test_config_full(name):
     check(spec, t, out, lse)
 
 
-def test_config2_sampled():
+def test_config2_all_queries():
+    """The document-QA tree, every query (every head): the root's pieces and every leaf."""
     spec = workloads.config("2")
     say(f"config 2: {spec.name}")
     t, plan, out, lse = run(spec)
-    check(spec, t, out, lse, queries=sample(64, 12))
+    check(spec, t, out, lse, by_node=True)
 
 
-def test_config4_sampled():
+def config4_queries(spec, extra=32, seed=1):
+    """One query per request (its deepest draft node, so the request's prefix
+    and its masked draft node are both checked) plus seeded random others."""
+    per_request = {}
+    for r, n in enumerate(spec.query_node):
+        per_request.setdefault(int(spec.parent[int(n)]), []).append(r)
+    chosen = set()
+    for rs in per_request.values():
+        chosen.add(max(rs, key=lambda r: bin(int(spec.query_mask[r])).count("1")))
+    chosen.update(sample(spec.num_queries, extra, seed))
+    return sorted(chosen)
+
+
+def test_config4_every_request():
     spec = workloads.config("4")
     say(f"config 4: {spec.name}")
     t, plan, out, lse = run(spec)
-    check(spec, t, out, lse, queries=sample(spec.num_queries, 48, 1))
+    queries = config4_queries(spec)
+    assert len({int(spec.parent[int(spec.query_node[r])]) for r in queries}) == 16
+    check(spec, t, out, lse, queries=queries)
 
 
-def test_config5_mqa_sampled():
+def test_config5_mqa_every_leaf():
     spec = workloads.config("5-mqa")
     say(f"config 5-mqa: {spec.name}")
     t, plan, out, lse = run(spec)
-    check(spec, t, out, lse, queries=sample(spec.num_queries, 24, 2))
+    check(spec, t, out, lse, queries=per_leaf_queries(spec), by_node=True)
 
 
-def test_config5_mha_sampled():
+def test_config5_mha_every_leaf():
     """The largest workload (MHA 32/32, ~38 GB of K/V: pool offsets beyond
-    2^32 bytes), in the launch configuration the bench times, on sampled
-    queries (every head)."""
+    2^32 bytes), in the launch configuration the bench times, on one query per
+    leaf (every head): every node and every piece lies on a checked path."""
     spec = workloads.config("5-mha")
     say(f"config 5-mha: {spec.name}, {spec.total_tokens} tokens")
     t, plan, out, lse = run(spec)
-    check(spec, t, out, lse, queries=sample(spec.num_queries, 8, 4))
+    queries = per_leaf_queries(spec)
+    say(f"  checking {len(queries)} queries (one per leaf)")
+    check(spec, t, out, lse, queries=queries, by_node=True)
     del t
 
 
@@ -459,6 +540,31 @@ def test_query_guided_baseline():
     check(spec, t, out, lse, queries=sample(128, 32, 3))
 
 
+@pytest.mark.parametrize("name", ["2", "3", "4"])
+def test_baseline_entry_point(name):
+    """pst_decode_attn_baseline (shared nodes read once per query) on the
+    document-QA, few-shot and speculative trees: against the oracle, and equal
+    to a query-guided plan run through pst_decode_attn."""
+    spec = workloads.config(name)
+    say(f"baseline entry point, config {name}: {spec.name}")
+    q, k, v = workloads.make_tensors(spec, "cuda")
+    tree = pst.Tree.from_spec(spec, out_dtype="f32")
+    out, lse = pst.decode_attn_baseline(tree, q, k, v)
+    out2, lse2 = pst.decode_attn_baseline(tree, q, k, v)  # the tree's plan, reused
+    plan = pst.Plan(tree, query_guided=True)
+    out3, lse3 = pst.decode_attn(plan, q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    assert torch.equal(out, out3) and torch.equal(lse, lse3)
+    if name == "4":
+        queries = config4_queries(spec, extra=16)
+    elif name == "2":
+        queries = list(range(spec.num_queries))
+    else:
+        queries = sample(spec.num_queries, 32, 3)
+    check(spec, (q, k, v), out, lse, queries=queries, by_node=name == "2")
+
+
 @pytest.mark.parametrize("kw", [dict(no_split=True), dict(fixed_chunk=256), dict(num_bins=1)])
 def test_plan_variants(kw):
     spec = workloads.config("3")
@@ -488,11 +594,45 @@ def test_plan_reuse_after_growth():
     check(grown, (q, k, v), out, lse, queries=[0, 126, 127])
 
 
-def test_peaked_attention_reported():
-    """Queries scaled by 8 make attention peaked; reported against the bf16 tolerance."""
+def test_peaked_attention():
+    """Queries scaled by 8 make attention peaked (a few tokens carry most of
+    the weight): the bf16 tolerance still holds."""
     spec = workloads.config("3")
     t, plan, out, lse = run(spec, q_scale=8.0)
-    check(spec, t, out, lse, queries=sample(128, 16, 5), tol=2e-2)
+    check(spec, t, out, lse, queries=sample(128, 16, 5))
+
+
+# (rows, V scale, V ramp along the piece (first, last factor))
+VSCALE_CASES = [
+    (4, 2.0 ** -12, None), (4, 2.0 ** 12, None),
+    (100, 2.0 ** -12, None), (100, 2.0 ** 12, None),
+    (256, 2.0 ** -12, None), (256, 2.0 ** 12, None),
+    (4, 1.0, (2.0 ** -20, 2.0 ** 10)),    # |V| grows along the piece: the fp16 scale is raised tile after tile
+    (100, 1.0, (2.0 ** -20, 2.0 ** 10)),
+    (256, 1.0, (2.0 ** -20, 2.0 ** 10)),
+    (256, 1.0, (2.0 ** 10, 2.0 ** -20)),  # |V| shrinks: later tiles convert below the first tile's scale
+    (16, 2.0 ** -60, None),
+    (16, 2.0 ** 60, None),
+]
+
+
+@pytest.mark.parametrize("rows,vscale,ramp", VSCALE_CASES)
+def test_v_magnitudes(rows, vscale, ramp):
+    """V far from unit scale, under peaked attention (q x 8), on one
+    1000-token node of `rows` MQA rows (every matrix-core layout): the
+    max-abs error stays within the bf16 tolerance relative to max|V|."""
+    spec = workloads.TreeSpec(f"vscale{rows}", np.array([-1]), np.array([1000]), np.array([0]), np.array([0]),
+                              rows, 1, 128, "bf16", 83)
+    q, k, v = workloads.make_tensors(spec, "cuda", q_scale=8.0)
+    f = torch.full((1000,), vscale, device="cuda", dtype=torch.float32)
+    if ramp is not None:
+        f = torch.logspace(math.log2(ramp[0]), math.log2(ramp[1]), 1000, base=2.0, device="cuda")
+    v = (v.float() * f[None, :, None]).to(torch.bfloat16).contiguous()
+    vmax = float(v.float().abs().max())
+    say(f"rows {rows}, V x {vscale:g}, ramp {ramp}, max|V| {vmax:.3e}")
+    t, plan, out, lse = run(spec, tensors=(q, k, v), num_bins=1)
+    assert plan.view()["b_eff"][0] == 1  # one piece: every raise of the scale happens inside it
+    check(spec, t, out, lse, tol=TOL["bf16"] * vmax, lse_tol=4 * TOL["bf16"])
 
 
 def test_empty_batch_and_single_token():
@@ -644,3 +784,19 @@ def test_decode_session_branch_prune():
         torch.cuda.synchronize()
         say(f"{op}: {sess.num_queries} queries, {len(kv_len)} nodes, {len(sess.free)} free pages")
         check(spec, (qs, kc, vc), out, lse)
+
+
+@pytest.mark.parametrize("rows", [4, 256])
+def test_v_zero_tiles_then_values(rows):
+    """The first 300 tokens of V are zero (the fp16 scale stays at its start
+    value over several tiles), then V ~ N(0, 1) x 2^20: the scale is raised
+    with O already accumulated."""
+    spec = workloads.TreeSpec(f"vzero{rows}", np.array([-1]), np.array([1000]), np.array([0]), np.array([0]),
+                              rows, 1, 128, "bf16", 85)
+    q, k, v = workloads.make_tensors(spec, "cuda", q_scale=4.0)
+    v = (v.float() * 2.0 ** 20).to(torch.bfloat16)
+    v[:, :300] = 0
+    v = v.contiguous()
+    vmax = float(v.float().abs().max())
+    t, plan, out, lse = run(spec, tensors=(q, k, v), num_bins=1)
+    check(spec, t, out, lse, tol=TOL["bf16"] * vmax, lse_tol=4 * TOL["bf16"])

@@ -518,3 +518,116 @@ def test_build_script_loads_without_the_package():
     assert r.returncode == 0, r.stderr
     src = open(os.path.join(root, "__graft_entry__.py")).read()
     assert "spec_from_file_location" in src and "from prefix_shared_tree_amd.build" not in src
+
+
+# ---------------------------------------------------------------------------
+# Fitted cost tables as shipped: the JSON loader and the plans the bench runs
+# ---------------------------------------------------------------------------
+
+TABLE_DIR = os.path.join(ROOT, "prefix_shared_tree_amd", "cost_tables")
+SHIPPED = sorted(f for f in os.listdir(TABLE_DIR) if f.startswith("gfx950_") and f.endswith(".json"))
+
+
+def _json_table(name):
+    import json
+
+    with open(os.path.join(TABLE_DIR, name)) as f:
+        d = json.load(f)
+    return d["rows_grid"], d["len_grid"], d["table_ns"]
+
+
+@pytest.mark.parametrize("name", SHIPPED)
+def test_cost_model_load_matches_the_file(name):
+    """pst_cost_model_load reads the shipped table: every lookup (grid points,
+    between them, below and beyond the grids) equals the oracle's lookup on
+    the arrays Python's own JSON reader finds in the file."""
+    lib = pst.CostModel.load(os.path.join(TABLE_DIR, name))
+    rg, lg, tb = _json_table(name)
+    ot = oracle.CostTable(rg, lg, tb)
+    for rows in [1, 2, 3, 7, 16, 31, 32, 100, 255, 256, 257, 1000]:
+        for L in [1, 15, 16, 17, 100, 1023, 1024, 1025, 40000, 65536, 65537, 300000]:
+            assert lib.lookup(rows, L) == ot.lookup(rows, L), (rows, L)
+
+
+@pytest.mark.parametrize("text,why", [
+    ("", "not an object"),
+    ("[1, 2]", "not an object"),
+    ('{"rows_grid": [1, 2], "len_grid": [16, 32]}', "no table"),
+    ('{"rows_grid": [1], "len_grid": [16, 32], "table_ns": [[5, 6]]} x', "trailing characters"),
+    ('{"rows_grid": [1], "len_grid": [16, 32], "table_ns": [[5, 6.5]]}', "fractional cost"),
+    ('{"rows_grid": [1, 2], "len_grid": [16, 32], "table_ns": [[5, 6]]}', "one table row missing"),
+    ('{"rows_grid": [1], "len_grid": [16, 32], "table_ns": [[5]]}', "short table row"),
+    ('{"rows_grid": [1], "len_grid": [16, 32], "table_ns": [[6, 5]]}', "decreasing costs"),
+    ('{"rows_grid": [2, 1], "len_grid": [16, 32], "table_ns": [[5, 6], [5, 6]]}', "rows grid not ascending"),
+    ('{"rows_grid": [1], "len_grid": [16, 32], "table_ns": [[5, 6]]', "unterminated object"),
+    ('{"rows_grid": [1], "len_grid": [16, 32], "table_ns": [[5, 6]], "note": "\\q"}', "bad escape"),
+])
+def test_cost_model_load_rejects(tmp_path, text, why):
+    path = tmp_path / "t.json"
+    path.write_text(text)
+    e = _raises("PST_E_INVALID_ARG", pst.CostModel.load, str(path))
+    assert "t.json" in str(e), why
+
+
+def test_cost_model_load_missing_file_and_extra_keys(tmp_path):
+    _raises("PST_E_INVALID_ARG", pst.CostModel.load, str(tmp_path / "absent.json"))
+    path = tmp_path / "ok.json"
+    path.write_text('{"note": {"a": [true, false, null, -1.5e3, "x\\u00e9"]}, "rows_grid": [1],'
+                    ' "len_grid": [16, 32], "table_ns": [[5, 9]], "raw_ns": [[1.25, 2]]}')
+    cm = pst.CostModel.load(str(path))
+    assert cm.lookup(1, 24) == 7 and cm.lookup(4, 48) == 13
+
+
+@pytest.mark.parametrize("name", SHIPPED)
+@pytest.mark.parametrize("cfg", ["1", "2", "3", "4", "5-mqa", "5-mha"])
+def test_plan_bit_exact_under_shipped_tables(name, cfg):
+    """The plans of the workloads under each shipped gfx950 table, with the
+    bins an MI355X gives (256 compute units, one PAC workgroup each, per kv
+    head), equal the oracle's plans bit for bit."""
+    spec = workloads.config(cfg)
+    m = max(1, 256 // spec.num_kv_heads)
+    r_max = 16 if spec.dtype == "f32" else 256
+    lib = pst.Plan(_tree(spec), pst.CostModel.load(os.path.join(TABLE_DIR, name)), num_bins=m, host_only=True)
+    got = lib.view()
+    want = oracle.plan(oracle.build_index(spec), spec.kv_len, spec.group, oracle.CostTable(*_json_table(name)), m,
+                       r_max=r_max)
+    assert np.array_equal(got["tasks"][:, :7], want["tasks"])
+    for key in ("bin_ptr", "slot_ptr", "entry_slot", "piece_len", "b_eff", "rows_per_group", "bin_load"):
+        assert np.array_equal(got[key], want[key].astype(got[key].dtype)), key
+    for key in ("makespan", "cost_l", "chosen_k", "num_slots"):
+        assert got[key] == want[key], key
+
+
+def test_baseline_entry_needs_a_device_tree():
+    import ctypes as C
+
+    t = _tree(workloads.config("1"))
+    dummy = C.c_void_p(4096)  # never dereferenced: the call fails before any launch
+    st = pst._lib.pst_decode_attn_baseline(t._h, None, dummy, dummy, dummy, dummy, None, dummy, 1 << 20, None)
+    assert pst.STATUS[st] == "PST_E_NO_DEVICE"
+    n = C.c_size_t()
+    assert pst.STATUS[pst._lib.pst_baseline_workspace_size(t._h, None, None, C.byref(n))] == "PST_E_NO_DEVICE"
+
+
+def test_pac_and_por_check_their_tensors():
+    """The per-phase calls check sizes, dtypes and devices like decode_attn:
+    the kernels size their reads from the plan, not from the tensors."""
+    import torch
+
+    t = _tree(workloads.config("1"))
+    p = pst.Plan(t, num_bins=4, host_only=True)
+    x = torch.zeros(4 * 4 * 64)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        pst.pac(p, x, x, x, ws)
+    with pytest.raises(ValueError):
+        pst.por(p, x, None, ws)
+
+
+def test_set_lengths_needs_one_length_per_node():
+    spec = workloads.config("3")
+    t = _tree(spec)
+    with pytest.raises(ValueError):
+        t.set_lengths(spec.kv_len[:-1])
+    with pytest.raises(ValueError):
+        t.set_lengths(np.concatenate([spec.kv_len, [5]]))
