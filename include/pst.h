@@ -345,6 +345,24 @@ pst_status pst_decode_attn_baseline(pst_tree_t tree, pst_cost_model_t cost, cons
                                     const void* v_pool, void* out, float* lse_out, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the hot
+ * path of pst_decode_attn with the partial outputs in a scratch array the
+ * library holds in device memory (PST_NOALLOC_SCRATCH_BYTES on every GPU it
+ * runs on, from the library's load until the process ends) instead of a
+ * caller workspace.  Allocates nothing: no hipMalloc, hipFree or allocating
+ * library call.  q, k_pool, v_pool, out and lse_out are as for
+ * pst_decode_attn, on the current device, which must be the plan's.
+ * PST_E_WORKSPACE (nothing launched) when the plan's partial outputs
+ * (pst_plan_workspace_size) exceed PST_NOALLOC_SCRATCH_BYTES.  Every call on
+ * one GPU uses that GPU's one array: calls that overlap on a GPU (other
+ * streams, other threads) race and must be serialised by the caller; the
+ * array keeps the last call's partials, and nothing in it needs clearing
+ * (every partial a call reads, the same call writes first). */
+#define PST_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+pst_status pst_decode_attn_noalloc(pst_plan_t plan, const void* q, const void* k_pool, const void* v_pool,
+                                   void* out, float* lse_out, void* stream);
+
 /* Release a tree, plan or cost model.  NULL is accepted.  A tree with live
  * plans (from pst_plan) is refused: free its plans first. */
 pst_status pst_free(void* obj);

@@ -56,7 +56,9 @@ EXPORTS = [
     "pst_cost_model_lookup", "pst_plan", "pst_plan_workspace_size", "pst_plan_get", "pst_decode_attn",
     "pst_pac", "pst_por", "pst_free", "pst_last_error", "pst_device_info", "pst_bench_flush",
     "pst_bench_read", "pst_cost_model_load", "pst_baseline_workspace_size", "pst_decode_attn_baseline",
+    "pst_decode_attn_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 128 << 20  # PST_NOALLOC_SCRATCH_BYTES
 
 
 class PstError(RuntimeError):
@@ -123,6 +125,7 @@ _sig = {
     "pst_cost_model_load": [C.c_char_p, C.POINTER(_P)],
     "pst_baseline_workspace_size": [_P, _P, _P, C.POINTER(C.c_size_t)],
     "pst_decode_attn_baseline": [_P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P],
+    "pst_decode_attn_noalloc": [_P, _P, _P, _P, _P, _P, _P],
 }
 for _name, _args in _sig.items():
     _f = getattr(_lib, _name)
@@ -465,6 +468,16 @@ def decode_attn_baseline(tree: Tree, q, k_pool, v_pool, *, cost=None, out=None, 
     _check_tensors(tree, q, k_pool, v_pool, out, lse)
     _check(_lib.pst_decode_attn_baseline(tree._h, ch, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse),
                                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out, lse
+
+
+def decode_attn_noalloc(plan: Plan, q, k_pool, v_pool, *, out, lse=None, stream=None):
+    """``pst_decode_attn_noalloc``: the hot path with the partial outputs in
+    the library's per-device scratch array instead of a workspace.  The C
+    call allocates nothing; the caller passes the outputs."""
+    _check_tensors(plan.tree, q, k_pool, v_pool, out, lse)
+    _check(_lib.pst_decode_attn_noalloc(plan._h, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse),
+                                        _stream(stream)))
     return out, lse
 
 

@@ -223,6 +223,24 @@ static pst_status check_shape(const pst_shape& s) {
   return PST_OK;
 }
 
+namespace pst {
+pst_status plan_ready_for_launch(pst_plan_t p) {
+  if (!p || p->magic != kPlanMagic) {
+    set_error("bad plan");
+    return PST_E_INVALID_ARG;
+  }
+  if (!p->on_device || !p->tree->on_device) {
+    set_error("plan or tree was built host-only");
+    return PST_E_NO_DEVICE;
+  }
+  if (p->generation != p->tree->generation) {
+    set_error("plan is stale: its tree changed");
+    return PST_E_PLAN_STALE;
+  }
+  return PST_OK;
+}
+}  // namespace pst
+
 extern "C" {
 
 const char* pst_last_error(void) { return g_last_error.c_str(); }
@@ -784,18 +802,8 @@ pst_status pst_plan_get(pst_plan_t p, pst_plan_view* v) {
 }
 
 static pst_status check_run(pst_plan_t p, const void* ws, size_t ws_bytes) {
-  if (!p || p->magic != kPlanMagic) {
-    set_error("bad plan");
-    return PST_E_INVALID_ARG;
-  }
-  if (!p->on_device || !p->tree->on_device) {
-    set_error("plan or tree was built host-only");
-    return PST_E_NO_DEVICE;
-  }
-  if (p->generation != p->tree->generation) {
-    set_error("plan is stale: its tree changed");
-    return PST_E_PLAN_STALE;
-  }
+  pst_status st = plan_ready_for_launch(p);
+  if (st != PST_OK) return st;
   size_t ob = 0, need = 0;
   workspace_layout(p, &ob, &need);
   if (need > 0 && (!ws || ws_bytes < need)) {

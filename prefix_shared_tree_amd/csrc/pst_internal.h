@@ -157,6 +157,10 @@ struct PorParams {
   int32_t hq;
 };
 
+// The checks every launch makes first (a valid plan, built for the device,
+// not stale); PST_OK or an error with set_error().
+pst_status plan_ready_for_launch(pst_plan_t plan);
+
 // Kernel launchers (defined in the .hip sources).  Return hipError_t as int.
 int launch_pac(const PacParams& p, int in_dtype, int head_dim, void* stream);
 int launch_por(const PorParams& p, int head_dim, int out_dtype, void* stream);

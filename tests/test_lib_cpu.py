@@ -631,3 +631,18 @@ def test_set_lengths_needs_one_length_per_node():
         t.set_lengths(spec.kv_len[:-1])
     with pytest.raises(ValueError):
         t.set_lengths(np.concatenate([spec.kv_len, [5]]))
+
+
+def test_noalloc_limit_and_host_only_plans():
+    """The binding's copy of PST_NOALLOC_SCRATCH_BYTES is the header's, and the
+    allocation-free entry point refuses host-only plans before any device call."""
+    import ctypes as C
+
+    with open(os.path.join(ROOT, "include", "pst.h")) as f:
+        m = re.search(r"#define PST_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == pst.NOALLOC_SCRATCH_BYTES
+    t = _tree(workloads.config("1"))
+    p = pst.Plan(t, num_bins=4, host_only=True)
+    dummy = C.c_void_p(4096)  # never dereferenced
+    st = pst._lib.pst_decode_attn_noalloc(p._h, dummy, dummy, dummy, dummy, None, None)
+    assert pst.STATUS[st] == "PST_E_NO_DEVICE"
