@@ -167,6 +167,25 @@ pst_status pst_tree_build(const pst_tree_desc* desc, const pst_shape* shape, uin
  * added, allocates the staging memory). */
 pst_status pst_tree_set_lengths(pst_tree_t tree, const int32_t* kv_len, void* stream);
 
+/* One decode step of growth with its K/V (DEFT section A.1: each request's
+ * tree grows by the token it just decoded; CoDec, implementation section:
+ * the partition is reused across steps).  nodes: host int32 [n], distinct;
+ * node nodes[i] gains one token whose K and V are row i of k_new / v_new
+ * (device, [n][num_kv_heads][head_dim], in_dtype, contiguous).  The rows go
+ * to each node's next position in k_pool / v_pool (contiguous: kv_offset +
+ * kv_len; paged: through the page table), every kv head; the node grows by
+ * one and the live plans' last pieces with it, so the plans stay valid, as
+ * with pst_tree_set_lengths.  Everything is checked first and nothing
+ * changes on an error (PST_E_INVALID_ARG: a node out of range or listed
+ * twice; PST_E_INVALID_TREE: a node would outgrow its pages or the pools, or
+ * a masked node pass 64 tokens; PST_E_UNSUPPORTED: a flattened plan of the
+ * tree is live).  The pool tokens and the device words to update travel in
+ * the arguments of kernel launches on `stream` (one launch per 128 rows):
+ * no copy, no host wait; launches queued on `stream` afterwards see the new
+ * rows and lengths. */
+pst_status pst_tree_append(pst_tree_t tree, int32_t n, const int32_t* nodes, const void* k_new, const void* v_new,
+                           void* k_pool, void* v_pool, void* stream);
+
 /* Host views of the index, valid until the tree is freed. */
 typedef struct {
   int32_t num_nodes;
@@ -344,6 +363,17 @@ pst_status pst_baseline_workspace_size(pst_tree_t tree, pst_cost_model_t cost, v
 pst_status pst_decode_attn_baseline(pst_tree_t tree, pst_cost_model_t cost, const void* q, const void* k_pool,
                                     const void* v_pool, void* out, float* lse_out, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/* A decode step's new K/V rows into the pools (DEFT section A.1: a request's
+ * tree grows by the token it just decoded).  k_new, v_new: device,
+ * [n][num_kv_heads][head_dim] in_dtype, contiguous; rows: device int64 [n],
+ * the pool token each new row goes to (for a paged tree, page * page_size +
+ * slot); k_pool, v_pool: the tree's pools, layout from pst_shape.  One launch
+ * on `stream` writes every row of every kv head, K and V; rows outside
+ * [0, pool_tokens) are not written.  Lengths are not changed: follow with
+ * pst_tree_set_lengths. */
+pst_status pst_write_kv_rows(pst_tree_t tree, const void* k_new, const void* v_new, const int64_t* rows, int32_t n,
+                             void* k_pool, void* v_pool, void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the hot

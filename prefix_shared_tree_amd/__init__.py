@@ -56,7 +56,7 @@ EXPORTS = [
     "pst_cost_model_lookup", "pst_plan", "pst_plan_workspace_size", "pst_plan_get", "pst_decode_attn",
     "pst_pac", "pst_por", "pst_free", "pst_last_error", "pst_device_info", "pst_bench_flush",
     "pst_bench_read", "pst_cost_model_load", "pst_baseline_workspace_size", "pst_decode_attn_baseline",
-    "pst_decode_attn_noalloc",
+    "pst_decode_attn_noalloc", "pst_write_kv_rows", "pst_tree_append",
 ]
 NOALLOC_SCRATCH_BYTES = 128 << 20  # PST_NOALLOC_SCRATCH_BYTES
 
@@ -126,6 +126,8 @@ _sig = {
     "pst_baseline_workspace_size": [_P, _P, _P, C.POINTER(C.c_size_t)],
     "pst_decode_attn_baseline": [_P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P],
     "pst_decode_attn_noalloc": [_P, _P, _P, _P, _P, _P, _P],
+    "pst_write_kv_rows": [_P, _P, _P, _P, C.c_int32, _P, _P, _P],
+    "pst_tree_append": [_P, C.c_int32, _P, _P, _P, _P, _P, _P],
 }
 for _name, _args in _sig.items():
     _f = getattr(_lib, _name)
@@ -272,6 +274,25 @@ class Tree:
         if kv_len.shape != (self.num_nodes,):
             raise ValueError(f"kv_len needs one length per node ({self.num_nodes}), got shape {kv_len.shape}")
         _check(_lib.pst_tree_set_lengths(self._h, p, _stream(stream) if not self.host_only else C.c_void_p(0)))
+
+    def append(self, nodes, k_new, v_new, k_pool, v_pool, stream=None):
+        """``pst_tree_append``: node ``nodes[i]`` gains one token whose K/V are
+        ``k_new[i]``, ``v_new[i]`` ([n, H_kv, d] on the GPU), written at the
+        node's next position in the pools."""
+        import torch
+
+        nodes, p = _arr(nodes, np.int32)
+        idt = torch.float32 if self.in_dtype == PST_F32 else torch.bfloat16
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            _check_one(name, t, idt)
+            if t.numel() != len(nodes) * self.num_kv_heads * self.head_dim:
+                raise ValueError(f"{name} must hold [n, num_kv_heads, head_dim] elements")
+        for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
+            _check_one(name, t, idt)
+            if t.numel() < self.kv_extent:
+                raise ValueError(f"{name} holds fewer than the {self.kv_extent} elements the tree's layout addresses")
+        _check(_lib.pst_tree_append(self._h, len(nodes), p, _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                                    _stream(stream)))
 
     def free(self):
         if self._h:
@@ -479,6 +500,28 @@ def decode_attn_noalloc(plan: Plan, q, k_pool, v_pool, *, out, lse=None, stream=
     _check(_lib.pst_decode_attn_noalloc(plan._h, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse),
                                         _stream(stream)))
     return out, lse
+
+
+def write_kv_rows(tree: Tree, k_new, v_new, rows, k_pool, v_pool, stream=None):
+    """``pst_write_kv_rows``: new K/V rows ``k_new``, ``v_new`` [n, H_kv, d]
+    into pool tokens ``rows`` (int64 [n] on the GPU) of every kv head."""
+    import torch
+
+    idt = torch.float32 if tree.in_dtype == PST_F32 else torch.bfloat16
+    n = int(rows.numel())
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _check_one(name, t, idt)
+        if t.numel() != n * tree.num_kv_heads * tree.head_dim:
+            raise ValueError(f"{name} must hold [n, num_kv_heads, head_dim] = [{n}, {tree.num_kv_heads}, "
+                             f"{tree.head_dim}] elements")
+    _check_one("k_pool", k_pool, idt)
+    _check_one("v_pool", v_pool, idt)
+    if rows.dtype != torch.int64 or rows.device.type != "cuda" or not rows.is_contiguous():
+        raise ValueError("rows must be a contiguous int64 GPU tensor")
+    if k_pool.numel() < tree.kv_extent or v_pool.numel() < tree.kv_extent:
+        raise ValueError(f"K/V pools hold fewer than the {tree.kv_extent} elements the tree's layout addresses")
+    _check(_lib.pst_write_kv_rows(tree._h, _ptr(k_new), _ptr(v_new), _ptr(rows), n, _ptr(k_pool), _ptr(v_pool),
+                                  _stream(stream)))
 
 
 def baseline_workspace_bytes(tree: Tree, cost=None, stream=None) -> int:

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -331,12 +332,11 @@ pst_status pst_tree_build(const pst_tree_desc* desc, const pst_shape* shape, uin
   return PST_OK;
 }
 
-pst_status pst_tree_set_lengths(pst_tree_t t, const int32_t* kv_len, void* stream) {
-  if (!t || t->magic != kTreeMagic || !kv_len) {
-    set_error("bad tree or kv_len");
-    return PST_E_INVALID_ARG;
-  }
-  TreeIndex& ix = t->ix;
+// Growth checks shared by pst_tree_set_lengths and pst_tree_append: every
+// length >= the current one, masked nodes <= 64, every node inside its pages
+// or the pools, and no flattened plan live.
+static pst_status check_growth(const pst_tree_s* t, const int32_t* kv_len) {
+  const TreeIndex& ix = t->ix;
   for (const pst_plan_s* p : t->plans) {
     if (p->r.flat_chunk > 0) {
       set_error("a flattened plan of this tree is live: its chunks would move (free it, grow, plan again)");
@@ -362,6 +362,47 @@ pst_status pst_tree_set_lengths(pst_tree_t t, const int32_t* kv_len, void* strea
       return PST_E_INVALID_TREE;
     }
   }
+  return PST_OK;
+}
+
+// The host side of growth: visible counts, the index's lengths, and the host
+// copies of the plans' device tasks (the last piece of every node absorbs
+// its growth).
+static void apply_growth(pst_tree_s* t, const int32_t* kv_len) {
+  TreeIndex& ix = t->ix;
+  // Visible counts: every node on a path grows, except that a query's own
+  // masked node keeps its mask bits.
+  for (int32_t r = 0; r < ix.B; ++r) {
+    const int32_t own = ix.query_node[r];
+    int64_t vis = 0;
+    for (int32_t e = ix.qn_ptr[r]; e < ix.qn_ptr[r + 1]; ++e) {
+      const int32_t n = ix.qn_idx[e];
+      if (n == own && ix.masked[n] && ix.have_mask)
+        vis += __builtin_popcountll(ix.qmask[r]);
+      else
+        vis += kv_len[n];
+    }
+    ix.visible[r] = vis;
+  }
+  std::copy(kv_len, kv_len + ix.N, ix.kv_len.begin());
+  for (pst_plan_s* p : t->plans) {
+    for (size_t i = 0; i < p->r.tasks.size(); ++i) {
+      const Task& a = p->r.tasks[i];
+      if (!(a.flags & PST_TASK_LAST_PIECE)) continue;
+      const int32_t len = ix.kv_len[a.node] - a.kv_begin;
+      if (i < p->dev_tasks.size()) p->dev_tasks[i].kv_len = len;
+    }
+  }
+}
+
+pst_status pst_tree_set_lengths(pst_tree_t t, const int32_t* kv_len, void* stream) {
+  if (!t || t->magic != kTreeMagic || !kv_len) {
+    set_error("bad tree or kv_len");
+    return PST_E_INVALID_ARG;
+  }
+  TreeIndex& ix = t->ix;
+  pst_status st = check_growth(t, kv_len);
+  if (st != PST_OK) return st;
   // The device copies of the new lengths and of every plan's tasks leave from
   // a pinned staging buffer (so the copies are asynchronous: no host wait).
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -398,30 +439,7 @@ pst_status pst_tree_set_lengths(pst_tree_t t, const int32_t* kv_len, void* strea
       slot->bytes = need;
     }
   }
-  // Visible counts: every node on a path grows, except that a query's own
-  // masked node keeps its mask bits.
-  for (int32_t r = 0; r < ix.B; ++r) {
-    const int32_t own = ix.query_node[r];
-    int64_t vis = 0;
-    for (int32_t e = ix.qn_ptr[r]; e < ix.qn_ptr[r + 1]; ++e) {
-      const int32_t n = ix.qn_idx[e];
-      if (n == own && ix.masked[n] && ix.have_mask)
-        vis += __builtin_popcountll(ix.qmask[r]);
-      else
-        vis += kv_len[n];
-    }
-    ix.visible[r] = vis;
-  }
-  std::copy(kv_len, kv_len + ix.N, ix.kv_len.begin());
-  // The last piece of every node absorbs the growth: patch the plans' tasks.
-  for (pst_plan_s* p : t->plans) {
-    for (size_t i = 0; i < p->r.tasks.size(); ++i) {
-      const Task& a = p->r.tasks[i];
-      if (!(a.flags & PST_TASK_LAST_PIECE)) continue;
-      const int32_t len = ix.kv_len[a.node] - a.kv_begin;
-      if (i < p->dev_tasks.size()) p->dev_tasks[i].kv_len = len;
-    }
-  }
+  apply_growth(t, kv_len);
   if (slot) {
     size_t off = 0;
     std::memcpy(slot->host, ix.kv_len.data(), ix.N * sizeof(int32_t));
@@ -440,6 +458,86 @@ pst_status pst_tree_set_lengths(pst_tree_t t, const int32_t* kv_len, void* strea
     if (e == hipSuccess) e = hipEventRecord(slot->copied, s);
     t->staging_next = (t->staging_next + 1) % pst_tree_s::kLengthSlots;
     if (e != hipSuccess) return hip_fail("length upload", e);
+  }
+  return PST_OK;
+}
+
+pst_status pst_tree_append(pst_tree_t t, int32_t n, const int32_t* nodes, const void* k_new, const void* v_new,
+                           void* k_pool, void* v_pool, void* stream) {
+  if (!t || t->magic != kTreeMagic || n < 0 || (n > 0 && (!nodes || !k_new || !v_new || !k_pool || !v_pool))) {
+    set_error("bad tree, negative count or NULL argument");
+    return PST_E_INVALID_ARG;
+  }
+  TreeIndex& ix = t->ix;
+  std::vector<int32_t> lens(ix.kv_len);
+  std::vector<uint8_t> grown(ix.N, 0);
+  std::vector<int64_t> rows(n);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t node = nodes[i];
+    if (node < 0 || node >= ix.N) {
+      set_error("nodes[" + std::to_string(i) + "] out of range");
+      return PST_E_INVALID_ARG;
+    }
+    if (grown[node]) {
+      set_error("node " + std::to_string(node) + " listed twice");
+      return PST_E_INVALID_ARG;
+    }
+    grown[node] = 1;
+    lens[node] += 1;
+  }
+  pst_status st = check_growth(t, lens.data());  // every new token inside its node's pages or the pools
+  if (st != PST_OK) return st;
+  if (!t->on_device) {
+    set_error("tree was built host-only");
+    return PST_E_NO_DEVICE;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t node = nodes[i];
+    const int64_t pos = ix.kv_len[node];  // the new token's position in its node
+    rows[i] = ix.page_size > 0 ? static_cast<int64_t>(ix.page_idx[ix.page_ptr[node] + pos / ix.page_size]) * ix.page_size +
+                                     pos % ix.page_size
+                               : ix.kv_offset[node] + pos;
+  }
+  apply_growth(t, lens.data());
+  // The device words to set: the grown nodes' lengths, and the kv_len of
+  // every live plan's last pieces of those nodes.
+  std::vector<std::pair<int32_t*, int32_t>> sets;
+  for (int32_t i = 0; i < n; ++i) sets.push_back({t->d_node_len + nodes[i], lens[nodes[i]]});
+  for (pst_plan_s* p : t->plans) {
+    if (!p->on_device) continue;
+    for (size_t j = 0; j < p->r.tasks.size() && j < p->dev_tasks.size(); ++j) {
+      const Task& a = p->r.tasks[j];
+      if (!(a.flags & PST_TASK_LAST_PIECE) || !grown[a.node]) continue;
+      int32_t* field = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p->d_tasks + j) + offsetof(DevTask, kv_len));
+      sets.push_back({field, p->dev_tasks[j].kv_len});
+    }
+  }
+  const int eb = elem_bytes(t->shape.in_dtype);
+  AppendParams ap{};
+  ap.kv.hkv = t->shape.num_kv_heads;
+  ap.kv.chunks = t->shape.head_dim * eb / 16;
+  ap.kv.pool_tokens = t->pool_tokens;
+  ap.kv.stride_head_bytes = t->shape.kv_stride_head * eb;
+  ap.kv.stride_token_bytes = t->shape.kv_stride_token * eb;
+  ap.kv.k_pool = k_pool;
+  ap.kv.v_pool = v_pool;
+  const int64_t row_bytes = static_cast<int64_t>(ap.kv.hkv) * ap.kv.chunks * 16;
+  const int64_t nsets = static_cast<int64_t>(sets.size());
+  const int64_t launches = std::max((static_cast<int64_t>(n) + kAppendRows - 1) / kAppendRows,
+                                    (nsets + kAppendSets - 1) / kAppendSets);
+  for (int64_t L = 0; L < launches; ++L) {
+    const int64_t r0 = L * kAppendRows, s0 = L * kAppendSets;
+    ap.kv.n = std::max<int64_t>(0, std::min<int64_t>(kAppendRows, n - r0));
+    ap.kv.k_new = static_cast<const char*>(k_new) + r0 * row_bytes;
+    ap.kv.v_new = static_cast<const char*>(v_new) + r0 * row_bytes;
+    for (int64_t r = 0; r < ap.kv.n; ++r) ap.rows[r] = rows[r0 + r];
+    ap.n_sets = static_cast<int32_t>(std::max<int64_t>(0, std::min<int64_t>(kAppendSets, nsets - s0)));
+    for (int32_t k = 0; k < ap.n_sets; ++k) {
+      ap.set_addr[k] = sets[s0 + k].first;
+      ap.set_val[k] = sets[s0 + k].second;
+    }
+    int e = launch_append(ap, stream);
+    if (e != 0) return hip_fail("append launch", static_cast<hipError_t>(e));
   }
   return PST_OK;
 }
@@ -993,6 +1091,38 @@ pst_status pst_free(void* obj) {
   }
   set_error("pst_free: not a pst object");
   return PST_E_INVALID_ARG;
+}
+
+pst_status pst_write_kv_rows(pst_tree_t t, const void* k_new, const void* v_new, const int64_t* rows, int32_t n,
+                             void* k_pool, void* v_pool, void* stream) {
+  if (!t || t->magic != kTreeMagic) {
+    set_error("bad tree");
+    return PST_E_INVALID_ARG;
+  }
+  if (n < 0 || (n > 0 && (!k_new || !v_new || !rows || !k_pool || !v_pool))) {
+    set_error("negative row count or NULL tensor");
+    return PST_E_INVALID_ARG;
+  }
+  if (!t->on_device) {
+    set_error("tree was built host-only");
+    return PST_E_NO_DEVICE;
+  }
+  const int eb = elem_bytes(t->shape.in_dtype);
+  KvRowsParams kp{};
+  kp.k_new = k_new;
+  kp.v_new = v_new;
+  kp.rows = rows;
+  kp.n = n;
+  kp.hkv = t->shape.num_kv_heads;
+  kp.chunks = t->shape.head_dim * eb / 16;
+  kp.pool_tokens = t->pool_tokens;
+  kp.stride_head_bytes = t->shape.kv_stride_head * eb;
+  kp.stride_token_bytes = t->shape.kv_stride_token * eb;
+  kp.k_pool = k_pool;
+  kp.v_pool = v_pool;
+  int e = launch_write_rows(kp, stream);
+  if (e != 0) return hip_fail("row write launch", static_cast<hipError_t>(e));
+  return PST_OK;
 }
 
 pst_status pst_bench_flush(void* buf, size_t bytes, void* stream) {

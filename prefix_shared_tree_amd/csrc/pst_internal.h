@@ -157,6 +157,36 @@ struct PorParams {
   int32_t hq;
 };
 
+struct KvRowsParams {
+  const void* k_new;  // [n][hkv][chunks] 16-byte chunks
+  const void* v_new;
+  const int64_t* rows;  // [n] pool token of each new row
+  int64_t n;
+  int32_t hkv;
+  int32_t chunks;  // 16-byte chunks per row and head (head_dim * elem / 16)
+  int64_t pool_tokens;
+  int64_t stride_head_bytes;
+  int64_t stride_token_bytes;
+  void* k_pool;
+  void* v_pool;
+};
+int launch_write_rows(const KvRowsParams& p, void* stream);
+
+// One launch of pst_tree_append: the new rows' pool tokens and the device
+// words to set (lengths of the grown nodes, kv_len of the plans' last pieces)
+// travel in the kernel's arguments, so a decode step needs no copy.
+constexpr int kAppendRows = 128;
+constexpr int kAppendSets = 192;
+struct AppendParams {
+  KvRowsParams kv;  // kv.rows unused; kv.n rows of this launch
+  int32_t n_sets;
+  int64_t rows[kAppendRows];
+  int32_t* set_addr[kAppendSets];
+  int32_t set_val[kAppendSets];
+};
+static_assert(sizeof(AppendParams) <= 4096, "kernel arguments are limited to 4 KB");
+int launch_append(const AppendParams& p, void* stream);
+
 // The checks every launch makes first (a valid plan, built for the device,
 // not stale); PST_OK or an error with set_error().
 pst_status plan_ready_for_launch(pst_plan_t plan);

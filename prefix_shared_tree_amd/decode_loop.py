@@ -11,8 +11,8 @@ A session owns a paged K/V pool (page table as in ``pst_tree_desc``) with a
 free list of pages.  Every query's own node is a leaf that only that query
 extends, with spare pages reserved for growth.
 * ``append``: one token per query into its leaf's next slot; the lengths
-  change in place (``pst_tree_set_lengths``: the last piece of every grown
-  node absorbs the growth, so the plan stays valid); re-plan on a fixed
+  change in place (``pst_tree_append``: the last piece of every grown node
+  absorbs the growth, so the plan stays valid); re-plan on a fixed
   period (``replan_every`` steps; 0 = never).  With a flattened partition
   (``plan_kw={"flatten": S_t}``) every step plans again: growth moves the
   chunks.
@@ -89,12 +89,6 @@ class DecodeSession:
         self.v[:, ok] = v[:, src[ok]]
         self.plan_kw = dict(plan_kw or {})
         self.host_only = bool(host_only)
-        # Pinned staging for each step's new pool rows, used in turn (a copy
-        # from pinned memory does not wait for the device); a buffer is
-        # refilled once the copy queued from it has run.
-        self._rows_pinned = []
-        self._rows_done = []
-        self._rows_next = 0
         self.replan_every = int(replan_every)
         self.steps = 0
         self.steps_since_plan = 0
@@ -110,6 +104,11 @@ class DecodeSession:
         page_idx = np.asarray([x for p in self.pages for x in p], dtype=np.int32)
         return page_ptr, page_idx
 
+    def _leaf_capacity(self):
+        """Tokens each query's leaf can hold (its pages)."""
+        qn = self.query_node.astype(np.int64)
+        return (self.page_ptr[qn + 1] - self.page_ptr[qn]).astype(np.int64) * self.page_size
+
     def _rebuild(self):
         """A new tree and plan after a topology change."""
         hq, hkv, d, dtype, odt = self.heads
@@ -121,6 +120,7 @@ class DecodeSession:
                          head_dim=d, dtype=dtype, out_dtype=odt, page_size=self.page_size, page_ptr=self.page_ptr,
                          page_idx=self.page_idx, pool_tokens=self.pool_pages * self.page_size,
                          host_only=self.host_only)
+        self.leaf_cap = self._leaf_capacity()
         self._make_plan()
         self.steps_since_plan = 0
 
@@ -159,55 +159,38 @@ class DecodeSession:
         return pages * P + positions % P
 
     # -- steps ---------------------------------------------------------------
-    def _device_rows(self, rows):
-        """``rows`` (int64 numpy) on the pool's device, copied from pinned
-        memory without a host wait when the pool is on a GPU."""
-        import torch
-
-        if self.k.device.type != "cuda":
-            return torch.from_numpy(rows)
-        slots = 4
-        if not self._rows_pinned:
-            self._rows_pinned = [None] * slots
-            self._rows_done = [None] * slots
-        i = self._rows_next
-        self._rows_next = (i + 1) % slots
-        if self._rows_done[i] is not None:
-            self._rows_done[i].synchronize()  # the copy queued from this buffer `slots` steps ago
-        if self._rows_pinned[i] is None or self._rows_pinned[i].numel() < len(rows):
-            self._rows_pinned[i] = torch.empty(max(len(rows), 64), dtype=torch.int64, pin_memory=True)
-        buf = self._rows_pinned[i][:len(rows)]
-        buf.numpy()[:] = rows
-        out = buf.to(self.k.device, non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record()
-        self._rows_done[i] = ev
-        return out
-
     def append(self, k_new, v_new):
         """Append one token per query: ``k_new``, ``v_new`` are [B, H_kv, d].
-        Nothing here waits for the device: the new rows' pool positions and
-        the new lengths travel from pinned memory."""
+        On the GPU one library call (``pst_tree_append``) writes the rows at
+        each leaf's next position and grows the lengths and the plan's last
+        pieces, in one kernel launch and without waiting for the device."""
         qn = self.query_node.astype(np.int64)
         pos = self.kv_len[qn].astype(np.int64)
-        cap = np.asarray([len(self.pages[i]) for i in qn], dtype=np.int64) * self.page_size
-        if (pos + 1 > cap).any():
+        if (pos + 1 > self.leaf_cap).any():
             raise ValueError("a leaf has used its spare capacity (max_new_tokens)")
-        rows = self._device_rows(self.pool_rows(qn, pos))
-        self.k[:, rows] = k_new.transpose(0, 1).to(self.k.dtype)
-        self.v[:, rows] = v_new.transpose(0, 1).to(self.v.dtype)
-        self.kv_len[qn] += 1
-        self.steps += 1
-        self.steps_since_plan += 1
-        if self.plan_kw.get("flatten"):
+        flat = bool(self.plan_kw.get("flatten"))
+        if flat:
             # A flattened partition's chunks move when a node grows: plan again
             # every step (the tree refuses growth while such a plan is live).
             self.plan.free()
             self.plan = None
+        if self.k.device.type == "cuda":
+            self.tree.append(qn.astype(np.int32), k_new.to(self.k.dtype).contiguous(),
+                             v_new.to(self.v.dtype).contiguous(), self.k, self.v)
+            self.kv_len[qn] += 1
+        else:
+            import torch
+
+            rows = torch.from_numpy(self.pool_rows(qn, pos))
+            self.k[:, rows] = k_new.transpose(0, 1).to(self.k.dtype)
+            self.v[:, rows] = v_new.transpose(0, 1).to(self.v.dtype)
+            self.kv_len[qn] += 1
             self.tree.set_lengths(self.kv_len)
+        self.steps += 1
+        self.steps_since_plan += 1
+        if flat:
             self._replan()
             return
-        self.tree.set_lengths(self.kv_len)
         if self.replan_every and self.steps_since_plan >= self.replan_every:
             self._replan()
 

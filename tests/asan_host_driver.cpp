@@ -22,6 +22,8 @@ int launch_pac(const PacParams&, int, int, void*) { return 1; }
 int launch_por(const PorParams&, int, int, void*) { return 1; }
 int launch_flush(void*, size_t, void*) { return 1; }
 int launch_read(const void*, size_t, float*, void*) { return 1; }
+int launch_write_rows(const KvRowsParams&, void*) { return 1; }
+int launch_append(const AppendParams&, void*) { return 1; }
 int pac_blocks_per_cu(int, int, int*) { return 1; }
 size_t pac_lds_bytes() { return 0; }
 }  // namespace pst
@@ -201,6 +203,21 @@ static void valid_trees() {
     }
     EXPECT(pst_decode_attn_baseline(t, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr) ==
            PST_E_NO_DEVICE);
+    EXPECT(pst_write_kv_rows(t, nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr) == PST_E_NO_DEVICE);
+    {
+      // pst_tree_append's checks run before it asks for the device.
+      int dummy = 0;
+      std::vector<int32_t> all;
+      for (int32_t i = 0; i < d.num_nodes; ++i) all.push_back(i);
+      const pst_status a = pst_tree_append(t, static_cast<int32_t>(all.size()), all.data(), &dummy, &dummy, &dummy,
+                                           &dummy, nullptr);
+      EXPECT(a == PST_E_NO_DEVICE || a == PST_E_INVALID_TREE);  // full pages, masked nodes at 64, pool end
+      const int32_t twice[2] = {0, 0};
+      EXPECT(pst_tree_append(t, 2, twice, &dummy, &dummy, &dummy, &dummy, nullptr) == PST_E_INVALID_ARG);
+      const int32_t outside[1] = {d.num_nodes};
+      EXPECT(pst_tree_append(t, 1, outside, &dummy, &dummy, &dummy, &dummy, nullptr) == PST_E_INVALID_ARG);
+    }
+    EXPECT(pst_write_kv_rows(t, nullptr, nullptr, nullptr, -1, nullptr, nullptr, nullptr) == PST_E_INVALID_ARG);
     EXPECT(pst_free(t) == PST_OK);
   }
   EXPECT(pst_free(cost) == PST_OK);

@@ -800,3 +800,72 @@ def test_v_zero_tiles_then_values(rows):
     vmax = float(v.float().abs().max())
     t, plan, out, lse = run(spec, tensors=(q, k, v), num_bins=1)
     check(spec, t, out, lse, tol=TOL["bf16"] * vmax, lse_tol=4 * TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype,hkv,d", [("bf16", 8, 128), ("f32", 2, 64), ("bf16", 1, 64)])
+def test_write_kv_rows(dtype, hkv, d):
+    """pst_write_kv_rows puts row i of k_new/v_new at pool token rows[i] of
+    every kv head (as an index_put would) and leaves rows outside the pools alone."""
+    T = 300
+    spec = workloads.TreeSpec("rows", np.array([-1]), np.array([T]), np.array([0]), np.array([0]), hkv * 2, hkv, d,
+                              dtype, 91)
+    _, k, v = workloads.make_tensors(spec, "cuda")
+    tree = pst.Tree.from_spec(spec)
+    n = 7
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    kn = torch.randn((n, hkv, d), generator=g, device="cuda").to(k.dtype)
+    vn = torch.randn((n, hkv, d), generator=g, device="cuda").to(k.dtype)
+    rows = torch.tensor([5, 0, 299, 17, -1, 300, 123], dtype=torch.int64, device="cuda")
+    want_k, want_v = k.clone(), v.clone()
+    keep = (rows >= 0) & (rows < T)
+    want_k[:, rows[keep]] = kn[keep].transpose(0, 1)
+    want_v[:, rows[keep]] = vn[keep].transpose(0, 1)
+    pst.write_kv_rows(tree, kn, vn, rows, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(k, want_k) and torch.equal(v, want_v)
+
+
+@pytest.mark.parametrize("page_size", [0, 16])
+def test_tree_append_steps(page_size):
+    """pst_tree_append: five decode steps grow two leaves (contiguous pools
+    with room, or pages with a spare page each); after every step the plan,
+    made once, still gives the oracle's attention over the grown tree."""
+    lens = np.array([100, 30, 50])
+    off = np.array([0, 100, 200])
+    spec = workloads.TreeSpec("append", np.array([-1, 0, 0]), lens, off, np.array([1, 2, 1]), 8, 2, 128, "bf16", 93)
+    q, k, v = workloads.make_tensors(spec, "cuda", kv_tokens=300)
+    if page_size:
+        paged, kk, vv = workloads.page_pools(spec, k, v, page_size, spare_pages=1)
+        tree = pst.Tree.from_paged(spec, paged, out_dtype="f32")
+    else:
+        kk, vv = k, v
+        tree = pst.Tree.from_spec(spec, out_dtype="f32", pool_tokens=300)
+    plan = pst.Plan(tree, num_bins=3)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    cur = lens.copy()
+    for step in range(5):
+        kn = torch.randn((2, 2, 128), generator=g, device="cuda").to(torch.bfloat16)
+        vn = torch.randn((2, 2, 128), generator=g, device="cuda").to(torch.bfloat16)
+        tree.append([1, 2], kn, vn, kk, vv)
+        for j, node in enumerate((1, 2)):  # the contiguous mirror the oracle reads
+            k[:, off[node] + cur[node]] = kn[j]
+            v[:, off[node] + cur[node]] = vn[j]
+        cur[1:] += 1
+        out, lse = pst.decode_attn(plan, q, kk, vv)
+        torch.cuda.synchronize()
+        grown = workloads.TreeSpec("grown", spec.parent, cur.copy(), off, spec.query_node, 8, 2, 128, "bf16", 93)
+        check(grown, (q, k, v), out, lse)
+    assert tree.index()["visible"].tolist() == [int(cur[0] + cur[1]), int(cur[0] + cur[2]), int(cur[0] + cur[1])]
+    with pytest.raises(pst.PstError) as e:
+        tree.append([1, 1], kn, vn, kk, vv)
+    assert e.value.code == "PST_E_INVALID_ARG"
+    if page_size:
+        # Each leaf had one spare page of 16 tokens: 30 + 5 fits in 3 pages; 11 more tokens would not.
+        one = kn[:1].contiguous()
+        for _ in range(48 - 35):
+            tree.append([1], one, one, kk, vv)
+        with pytest.raises(pst.PstError) as e:
+            tree.append([1], one, one, kk, vv)
+        assert e.value.code == "PST_E_INVALID_TREE"
