@@ -502,7 +502,8 @@ GATE_CONFIGS = ("2", "3", "4")
 def gate(torch, pst, workloads, evict_bufs, a):
     """PAC + POR of the document-QA, few-shot and speculative trees, measured
     like the main line (cold caches, plan reused), against 8 TB/s on their
-    unique K/V bytes."""
+    unique K/V bytes; with each PAC launch's HBM traffic from the counter
+    summary while it matches the kernel."""
     rows = {}
     for name in GATE_CONFIGS:
         spec = workloads.config(name)
@@ -522,6 +523,8 @@ def gate(torch, pst, workloads, evict_bufs, a):
             "logical_tokens_per_s": st["logical_tokens"] / (ms * 1e-3),
             "unique_kv_GBps": st["unique_kv_bytes"] / (ms * 1e-3) / 1e9,
             "unique_kv_frac_of_peak": st["unique_kv_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "pac_unique_kv_frac_of_peak": st["unique_kv_bytes"] / (statistics.mean(pac) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "pac_traffic_bytes_per_launch": traffic_for(a.traffic, spec.name),
         }
         del q, k, v, tree, plan, ws, out, lse
         torch.cuda.empty_cache()
