@@ -64,6 +64,9 @@ def parse():
                          "cost-model plan")
     ap.add_argument("--page-size", type=int, default=0,
                     help="> 0: K/V in a paged pool of pages of this many tokens (scattered, with holes)")
+    ap.add_argument("--page-order", choices=["scattered", "sequential"], default="scattered",
+                    help="paged pool: pages drawn at random from a pool one eighth larger (scattered), or "
+                         "numbered in order without holes (sequential)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "pac_traffic.json"),
                     help="rocprofv3 counter summary giving the PAC kernel's HBM bytes")
     return ap.parse_args()
@@ -368,7 +371,8 @@ def main():
     # oracle sample reads the contiguous k, v.
     kk, vv, paged = k, v, None
     if a.page_size > 0:
-        paged, kk, vv = workloads.page_pools(spec, k, v, a.page_size, fill=0.0)
+        paged, kk, vv = workloads.page_pools(spec, k, v, a.page_size, fill=0.0,
+                                             scatter=a.page_order == "scattered")
     t0 = time.perf_counter()
     tree = pst.Tree.from_paged(spec, paged, out_dtype="f32") if paged else pst.Tree.from_spec(spec, out_dtype="f32")
     t_tree = (time.perf_counter() - t0) * 1e3
@@ -420,7 +424,7 @@ def main():
                    "head_dim": spec.head_dim, "nodes": spec.num_nodes, "queries": spec.num_queries,
                    "unique_kv_tokens": st["unique_kv_tokens"], "logical_tokens": st["logical_tokens"],
                    "cache": "cold (1 GiB read of an unrelated buffer before each step)", "plan_reused": True,
-                   "kv_layout": f"paged, {a.page_size}-token pages" if paged else "contiguous",
+                   "kv_layout": f"paged, {a.page_size}-token pages, {a.page_order}" if paged else "contiguous",
                    "partition": f"DEFT-Flatten, {a.flatten}-token chunks" if a.flatten else "cost model"},
         "unique_kv_GBps": st["unique_kv_bytes"] / (ms * 1e-3) / 1e9,
         "unique_kv_frac_of_peak": st["unique_kv_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,

@@ -168,7 +168,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, uint32
 // held in registers across every piece.
 __device__ __forceinline__ int piece_tid() {
   int t;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(static_cast<int>(threadIdx.x)));
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(static_cast<int>(__builtin_amdgcn_workitem_id_x())));
   return t;
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -230,30 +230,100 @@ struct TaskInfo {
   int flat0;          // flattened chunk: its first token in the row table
   int linear;         // flattened chunk over consecutive pool rows: addressed like a contiguous run
   int shared;         // other tasks (row groups, query-guided groups) read the same K/V tokens
+  int pg0;            // paged: the node's first entry in the page table
   const char* kbase;  // K of this kv head at the piece's first token (paged: at the pool's first row)
   const char* vbase;
 };
 
-// Paged K/V: the pool row of the first token of 1 KB DMA block b of `tile`,
-// and the valid tokens of that block (tpb tokens per block; a block never
-// crosses a page: pages hold a power of two >= 8 tokens and pieces start at
-// multiples of 64).  Page-table reads are scalar (wave-uniform indices).
-struct PagedBlock {
-  int64_t row;
-  int valid;
-};
-__device__ __forceinline__ PagedBlock paged_block(const PacParams& p, const TaskInfo& t, int tile_tok, int b,
-                                                  int tpb) {
-  const auto* ptr = (const __attribute__((address_space(4))) int32_t*)(p.page_ptr);
+// Paged K/V.  Nodes start on a page, pieces at multiples of 64 tokens of
+// their node and pages hold a power of two >= 8 tokens, so a 1 KB block
+// (TPB <= 8 tokens) never crosses a page.  A half-tile is fetched one of
+// three ways, the first that applies (wave-uniform, fixed per piece):
+//   whole tiles  pages hold whole tiles and the piece starts on a tile: one
+//                page per tile, blocks round-robin over the wavefronts;
+//   runs         each wavefront takes KB consecutive blocks on one page;
+//   blocks       (8-token pages under 8-token blocks) every block its own page.
+// Each way builds as few buffer descriptors as it can, with scalar
+// arithmetic, from the rows they start at; the lanes' offsets inside them
+// are the same in every tile.
+template <int TT>
+__device__ __forceinline__ bool paged_whole_tiles(const PacParams& p, const TaskInfo& t) {
+  return (1 << p.page_shift) >= TT && (t.kv_begin & (TT - 1)) == 0;
+}
+// Page of the token ft tokens into the piece (for a token past the piece's
+// end, a page of the node: such blocks read nothing).
+__device__ __forceinline__ int page_of(const PacParams& p, const TaskInfo& t, int ft) {
   const auto* idx = (const __attribute__((address_space(4))) int32_t*)(p.page_idx);
-  const int tb = tile_tok + b * tpb;  // first token of the block, from the piece start
-  PagedBlock r;
-  r.valid = max(0, min(tpb, t.kv_len - tb));
-  const int pos = t.kv_begin + tb;  // position in the node
-  // A block past the piece's end reads nothing; it still names a valid page.
-  const int slot = ptr[t.node] + (r.valid > 0 ? (pos >> p.page_shift) : 0);
-  r.row = (static_cast<int64_t>(idx[slot]) << p.page_shift) + (pos & ((1 << p.page_shift) - 1));
-  return r;
+  return idx[t.pg0 + ((t.kv_begin + (ft < t.kv_len ? ft : 0)) >> p.page_shift)];
+}
+// Byte offset, from the kv head's first row, of the token ft tokens into the
+// piece, which lies on page `page`.
+__device__ __forceinline__ int64_t paged_off(const PacParams& p, const TaskInfo& t, int64_t stb, int ft, int page) {
+  return ((static_cast<int64_t>(page) << p.page_shift) + ((t.kv_begin + ft) & ((1 << p.page_shift) - 1))) * stb;
+}
+// Offset of lane `lane`'s chunk of block b inside a descriptor that starts
+// `lead` tokens before the block: token lane / CPT of the block, chunk
+// (lane % CPT) ^ (token % CPT), the token counted from the tile's start (the
+// swizzle of the LDS tile).
+template <int CPT, int TPB>
+__device__ __forceinline__ int block_voff(int b, int lead, int lane, int64_t stb) {
+  const int lt = lane / CPT, phys = lane % CPT;
+  return static_cast<int>((lead + lt) * stb) + ((phys ^ ((b * TPB + lt) & (CPT - 1))) << 4);
+}
+// The page numbers a wavefront's share of a paged half-tile needs: the
+// tile's page (whole tiles), its run's page (runs), or its two blocks' pages.
+// Scalar reads; K and V of a tile take the same.
+struct PgPre {
+  int a, b;
+};
+template <int D, int EB, int NW>
+__device__ __forceinline__ PgPre pg_fetch(const PacParams& p, const TaskInfo& t, int tile, int w) {
+  using G = Geo<D, EB>;
+  constexpr int TPB = 64 / G::CPT, KB = TILE_BYTES / 1024 / NW;
+  if (p.page_shift < 0) return PgPre{0, 0};
+  const int tok_base = tile * G::TT;
+  if (paged_whole_tiles<G::TT>(p, t)) {
+    const int a = page_of(p, t, tok_base);
+    return PgPre{a, a};
+  }
+  const int ft = tok_base + KB * w * TPB;
+  const int a = page_of(p, t, ft);
+  return PgPre{a, (1 << p.page_shift) >= KB * TPB ? a : page_of(p, t, ft + TPB)};
+}
+// The DMA operations of this wavefront for a paged half-tile: emit(off,
+// bytes, voff, b) per operation, for block b, with a descriptor from byte
+// `off` of the kv head over `bytes` bytes and the lane's offset voff in it.
+template <int D, int EB, int NW, typename Emit>
+__device__ __forceinline__ void paged_half(const PacParams& p, const TaskInfo& t, int64_t stb, int tile, int lane,
+                                           int w, const PgPre& pg, Emit&& emit) {
+  using G = Geo<D, EB>;
+  constexpr int TPB = 64 / G::CPT, KB = TILE_BYTES / 1024 / NW;
+  const int tok_base = tile * G::TT;
+  if (paged_whole_tiles<G::TT>(p, t)) {
+    const int64_t off = paged_off(p, t, stb, tok_base, pg.a);
+    const int64_t bytes = static_cast<int64_t>(min(G::TT, t.kv_len - tok_base)) * stb;
+#pragma unroll
+    for (int c = 0; c < KB; ++c) {
+      const int b = c * NW + w;
+      emit(off, bytes, block_voff<G::CPT, TPB>(b, b * TPB, lane, stb), b);
+    }
+    return;
+  }
+  const int ft = tok_base + KB * w * TPB;  // the wavefront's first token
+  if ((1 << p.page_shift) >= KB * TPB) {
+    const int64_t off = paged_off(p, t, stb, ft, pg.a);
+    const int64_t bytes = static_cast<int64_t>(min(max(t.kv_len - ft, 0), KB * TPB)) * stb;
+#pragma unroll
+    for (int c = 0; c < KB; ++c) emit(off, bytes, block_voff<G::CPT, TPB>(KB * w + c, c * TPB, lane, stb), KB * w + c);
+    return;
+  }
+#pragma unroll
+  for (int c = 0; c < KB; ++c) {
+    const int fb = ft + c * TPB;
+    const int64_t off = paged_off(p, t, stb, fb, c == 0 ? pg.a : pg.b);
+    const int64_t bytes = static_cast<int64_t>(min(max(t.kv_len - fb, 0), TPB)) * stb;
+    emit(off, bytes, block_voff<G::CPT, TPB>(KB * w + c, 0, lane, stb), KB * w + c);
+  }
 }
 
 // Row r of the task -> (query entry, q-head); returns false past the task's rows.
@@ -347,37 +417,17 @@ __device__ __forceinline__ void issue_tile(const PacParams& p, const TaskInfo& t
     }
     return;
   }
-  if (p.page_shift >= 0 && ((1 << p.page_shift) < G::TT || (t.kv_begin & (G::TT - 1)) != 0)) {
-    // Pages shorter than a tile, or a piece that starts off a tile boundary
-    // of its node (64-token piece starts with 128-token tiles), so that a
-    // tile may cross a page: consecutive blocks per wavefront, sharing one
-    // page number when a page holds their tokens (see issue_half).
-    const bool shared = (1 << p.page_shift) >= KB * TPB;
-    PagedBlock pw{};
-    if (shared) pw = paged_block(p, t, tok_base, w, KB * TPB);
-#pragma unroll
-    for (int c = 0; c < KB; ++c) {
-      const int b = KB * w + c;
-      const PagedBlock pb = shared ? pw : paged_block(p, t, tok_base, b, TPB);
-      const int first = shared ? KB * w * TPB : b * TPB;  // first token the descriptor starts at
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(t.kbase + pb.row * stb, pb.valid * stb);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(t.vbase + pb.row * stb, pb.valid * stb);
-      const int P = b * 64 + lane;
-      const int tok = P / G::CPT, phys = P % G::CPT;
-      const int voff = static_cast<int>((tok - first) * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4);
-      dma16(rk, voff, lds_addr(st + b * 1024));
-      dma16(rv, voff, lds_addr(st + TILE_BYTES + b * 1024));
-    }
+  if (p.page_shift >= 0) {
+    // Paged: K and V of a block sit at the same rows.
+    const PgPre pg = pg_fetch<D, EB, NW>(p, t, tile, w);
+    paged_half<D, EB, NW>(p, t, stb, tile, lane, w, pg, [&](int64_t off, int64_t bytes, int voff, int b) {
+      dma16(make_rsrc(t.kbase + off, bytes), voff, lds_addr(st + b * 1024));
+      dma16(make_rsrc(t.vbase + off, bytes), voff, lds_addr(st + TILE_BYTES + b * 1024));
+    });
     return;
   }
   const char* kb = t.kbase + tok_base * stb;
   const char* vb = t.vbase + tok_base * stb;
-  if (p.page_shift >= 0) {
-    // Pages of at least a tile and a tile-aligned piece: the tile lies in one page.
-    const PagedBlock pb = paged_block(p, t, tok_base, 0, 1);
-    kb = t.kbase + pb.row * stb;
-    vb = t.vbase + pb.row * stb;
-  }
   const int64_t bytes = static_cast<int64_t>(min(G::TT, t.kv_len - tok_base)) * stb;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, bytes);
@@ -456,22 +506,22 @@ __device__ __forceinline__ char* kslot(int j) { return pac_lds + (j % NSTAGE) * 
 __device__ __forceinline__ char* vslot(int j) { return pac_lds + (j % NSTAGE) * STAGE_BYTES + TILE_BYTES; }
 
 // Which 1 KB blocks of a K or V half a wavefront's DMA fills: runs of
-// kHalfOps consecutive blocks per wavefront when each block finds its own
-// rows (flattened chunks; paged tiles that may cross a page), else
-// round-robin over the wavefronts.  Wave-uniform.
+// kHalfOps consecutive blocks per wavefront when blocks find their own rows
+// (flattened chunks; paged tiles that may cross a page), else round-robin
+// over the wavefronts.  Wave-uniform.
 template <int D>
 __device__ __forceinline__ bool half_in_runs(const PacParams& p, const TaskInfo& t) {
   using G = Geo<D, 2>;
-  return (p.mask_words > 0 && !t.linear) ||
-         (p.page_shift >= 0 && ((1 << p.page_shift) < G::TT || (t.kv_begin & (G::TT - 1)) != 0));
+  return (p.mask_words > 0 && !t.linear) || (p.page_shift >= 0 && !paged_whole_tiles<G::TT>(p, t));
 }
 
 // DMA of the K (or V) half of tile `tile` (16 KB) into `dst`: every wavefront
 // writes kHalfOps 1 KB blocks; lane L of block b fills chunk position
-// P = 64 b + L, i.e. token P / CPT, chunk (P % CPT) ^ (token % CPT).
+// P = 64 b + L, i.e. token P / CPT, chunk (P % CPT) ^ (token % CPT).  `pg`:
+// the tile's page numbers (paged pieces; see pg_fetch).
 template <int D, int NW, bool NT>
 __device__ __forceinline__ void issue_half(const PacParams& p, const TaskInfo& t, const char* base, int64_t stb,
-                                           int tile, char* dst, int tid) {
+                                           int tile, char* dst, int tid, const PgPre& pg) {
   using G = Geo<D, 2>;
   constexpr int TPB = 64 / G::CPT;  // tokens per 1 KB block
   const int tok_base = tile * G::TT;
@@ -490,45 +540,13 @@ __device__ __forceinline__ void issue_half(const PacParams& p, const TaskInfo& t
     }
     return;
   }
-  if (half_in_runs<D>(p, t)) {
-    // Pages shorter than a tile, or a piece that starts off a tile boundary
-    // of its node (so a tile may cross a page): this wavefront takes the consecutive blocks
-    // kHalfOps w .. kHalfOps w + kHalfOps - 1, which share one page when a
-    // page holds at least their tokens (one page number and one descriptor),
-    // else each block looks up its own.
-    constexpr int KB = kHalfOps<NW>;
-    if ((1 << p.page_shift) >= KB * TPB) {
-      const PagedBlock pb = paged_block(p, t, tok_base, w, KB * TPB);
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(base + pb.row * stb, pb.valid * stb);
-#pragma unroll
-      for (int c = 0; c < KB; ++c) {
-        const int b = KB * w + c;
-        const int P = b * 64 + lane;
-        const int tok = P / G::CPT, phys = P % G::CPT;
-        dma16<NT>(r, static_cast<int>((tok - KB * w * TPB) * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4),
-              lds_addr(dst + b * 1024));
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < KB; ++c) {
-        const int b = KB * w + c;
-        const PagedBlock pb = paged_block(p, t, tok_base, b, TPB);
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + pb.row * stb, pb.valid * stb);
-        const int P = b * 64 + lane;
-        const int tok = P / G::CPT, phys = P % G::CPT;
-        dma16<NT>(r, static_cast<int>((tok - b * TPB) * stb) + ((phys ^ (tok & (G::CPT - 1))) << 4),
-              lds_addr(dst + b * 1024));
-      }
-    }
+  if (p.page_shift >= 0) {
+    paged_half<D, 2, NW>(p, t, stb, tile, lane, w, pg, [&](int64_t off, int64_t bytes, int voff, int b) {
+      dma16<NT>(make_rsrc(base + off, bytes), voff, lds_addr(dst + b * 1024));
+    });
     return;
   }
   const char* tbase = base + tok_base * stb;
-  if (p.page_shift >= 0) {
-    // Pages of at least a tile and a piece that starts on a tile boundary:
-    // the tile lies in one page, so one page number serves it.
-    const PagedBlock pb = paged_block(p, t, tok_base, 0, 1);
-    tbase = base + pb.row * stb;
-  }
   const int64_t bytes = static_cast<int64_t>(min(G::TT, t.kv_len - tok_base)) * stb;
   const __amdgpu_buffer_rsrc_t r = make_rsrc(tbase, bytes);
 #pragma unroll
@@ -625,11 +643,28 @@ __device__ __forceinline__ bool mfma_piece(const PacParams& p, const TaskInfo& t
       if (o * NW + w < qops_total) dma16(rq, static_cast<int>(qoff[o]), lds_addr(qarea + (o * NW + w) * 1024));
   }
   if (p.mask_words > 0) issue_masks<NW>(p, t, tid);
-  if (0 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, 0, kslot(0), tid);
-  if (1 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, 1, kslot(1), tid);
-  if (0 < nt) issue_half<D, NW, NT>(p, t, t.vbase, stb, 0, vslot(0), tid);
-  if (2 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, 2, kslot(2), tid);
-  if (1 < nt) issue_half<D, NW, NT>(p, t, t.vbase, stb, 1, vslot(1), tid);
+  // Paged pieces: the page numbers of the next K refill (pg_cur) and of the
+  // next V refill (pg_prev, the K refill's of one iteration earlier), read
+  // one refill ahead of their use.
+  PgPre pg_prev, pg_cur;
+  {
+    const PgPre pg0 = pg_fetch<D, 2, NW>(p, t, 0, w), pg1 = pg_fetch<D, 2, NW>(p, t, 1, w);
+    pg_prev = pg_fetch<D, 2, NW>(p, t, 2, w);
+    if (0 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, 0, kslot(0), tid, pg0);
+    if (1 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, 1, kslot(1), tid, pg1);
+    if (0 < nt) issue_half<D, NW, NT>(p, t, t.vbase, stb, 0, vslot(0), tid, pg0);
+    if (2 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, 2, kslot(2), tid, pg_prev);
+    if (1 < nt) issue_half<D, NW, NT>(p, t, t.vbase, stb, 1, vslot(1), tid, pg1);
+    pg_cur = pg_fetch<D, 2, NW>(p, t, 3, w);
+  }
+  // The refills of one iteration: K of tile j and V of tile j - 1 (those
+  // within the piece); then the pages move one tile on.
+  auto refill_kv = [&](int j) {
+    if (j < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, j, kslot(j), tid, pg_cur);
+    if (j - 1 < nt) issue_half<D, NW, NT>(p, t, t.vbase, stb, j - 1, vslot(j - 1), tid, pg_prev);
+    pg_prev = pg_cur;
+    pg_cur = pg_fetch<D, 2, NW>(p, t, j + 1, w);
+  };
 
   bf16x8 qf[RBR][KS];
   f32x4 o[DB][RBR];
@@ -727,8 +762,13 @@ __device__ __forceinline__ bool mfma_piece(const PacParams& p, const TaskInfo& t
       // and eight wavefronts issuing together right after a barrier queue up
       // behind each other.  (Bandwidth-bound layouts refill at the barrier,
       // as early as possible.)
-      if (kSpread && sb == 0 && tile + 3 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, tile + 3, kslot(tile + 3), tid);
-      if (kSpread && sb == NSUB - 1 && tile + 2 < nt) issue_half<D, NW, NT>(p, t, t.vbase, stb, tile + 2, vslot(tile + 2), tid);
+      if (kSpread && sb == 0 && tile + 3 < nt)
+        issue_half<D, NW, NT>(p, t, t.kbase, stb, tile + 3, kslot(tile + 3), tid, pg_cur);
+      if (kSpread && sb == NSUB - 1) {
+        if (tile + 2 < nt) issue_half<D, NW, NT>(p, t, t.vbase, stb, tile + 2, vslot(tile + 2), tid, pg_prev);
+        pg_prev = pg_cur;
+        pg_cur = pg_fetch<D, 2, NW>(p, t, tile + 4, w);
+      }
       if constexpr (!kSpread) pv(vslot(tile - 1), ts, sb);
     }
     // Raw scores; lane holds tokens 4 lg + i of each 16-token block, row l16.
@@ -951,10 +991,7 @@ __device__ __forceinline__ bool mfma_piece(const PacParams& p, const TaskInfo& t
     // K of tile i - 1 and V of tile i - 2 are finished: refill them (here, or
     // in the steps of tile i when `refill` is false; at i = 0 the refill
     // targets hold the queries: after the reads below).
-    if (i > 0 && refill) {
-      if (i + 3 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, i + 3, kslot(i + 3), tid);
-      if (i + 2 < nt) issue_half<D, NW, NT>(p, t, t.vbase, stb, i + 2, vslot(i + 2), tid);
-    }
+    if (i > 0 && refill) refill_kv(i + 3);
     if (i == 0) {
       if (active) {
 #pragma unroll
@@ -972,8 +1009,7 @@ __device__ __forceinline__ bool mfma_piece(const PacParams& p, const TaskInfo& t
       wait_lds_all();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (3 < nt) issue_half<D, NW, NT>(p, t, t.kbase, stb, 3, kslot(3), tid);
-      if (2 < nt) issue_half<D, NW, NT>(p, t, t.vbase, stb, 2, vslot(2), tid);
+      refill_kv(3);
     }
   };
   // The NSUB steps of tile i (tile 0: no products of a previous tile).
@@ -1348,25 +1384,35 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
 
 // LAYOUT selects the instantiation (kContig, kPaged, kFlat); each is
 // compiled without the other layouts' addressing code (its registers and
-// scalar registers stay with the tile loop).
-template <typename T, int D, int LAYOUT>
+// scalar registers stay with the tile loop).  DOT: the kernel holds the
+// dot-product path (float inputs; bf16 plans that send small pieces there).
+// The bf16 kernels of the other plans leave it out: its code, inlined
+// beside the matrix-core loops, costs them registers and schedule.
+template <typename T, int D, int LAYOUT, bool DOT>
 __global__ __launch_bounds__(kWaves<T> * 64) __attribute__((amdgpu_waves_per_eu(kWaves<T> / 4, kWaves<T> / 4)))
 void pac_kernel(PacParams p) {
   constexpr int NW = kWaves<T>;
-  if constexpr (LAYOUT != kPaged) p.page_shift = -1;  // every page-table branch folds away
+  if constexpr (LAYOUT != kPaged)
+    p.page_shift = -1;  // every page-table branch folds away
+  else
+    __builtin_assume(p.page_shift >= 3 && p.page_shift <= 16);  // and every contiguous one
   if constexpr (LAYOUT != kFlat)
     p.mask_words = 0;  // and every row-table branch
   else
     __builtin_assume(p.mask_words > 0);
-  const int bin = blockIdx.x % p.num_bins;
-  const int kvh = blockIdx.x / p.num_bins;
+  // The work-group and work-item ids are read with the intrinsics: in a
+  // kernel this large the library accessors stay out-of-line calls, whose
+  // calling convention pushes the kernel arguments out of scalar registers.
+  const int wg = static_cast<int>(__builtin_amdgcn_workgroup_id_x());
+  const int bin = wg % p.num_bins;
+  const int kvh = wg / p.num_bins;
   const int tb = p.bin_ptr[bin], te = p.bin_ptr[bin + 1];
   const int64_t esz = sizeof(T);
   // The next piece's record travels one dword per lane (lanes 0..11 of every
   // wavefront) while the current piece runs, and is handed over through LDS.
   constexpr int TW = sizeof(DevTask) / 4;
   uint32_t* const task_lds = reinterpret_cast<uint32_t*>(pac_lds + kAuxOff + kAuxBytes - sizeof(DevTask));
-  const int tid = threadIdx.x;
+  const int tid = static_cast<int>(__builtin_amdgcn_workitem_id_x());
   if (tb < te && tid < TW) task_lds[tid] = reinterpret_cast<const uint32_t*>(p.tasks + tb)[tid];
   __syncthreads();
   int ev_carry = kEvStart;  // the V scale exponent the next matrix-core piece starts from
@@ -1393,6 +1439,7 @@ void pac_kernel(PacParams p) {
     t.flat0 = static_cast<int>(tok0);
     t.linear = (__builtin_amdgcn_readfirstlane(task.flags) & kDevLinear) != 0;
     t.shared = (__builtin_amdgcn_readfirstlane(task.flags) & kDevShared) != 0;
+    t.pg0 = p.page_shift >= 0 ? ((const __attribute__((address_space(4))) int32_t*)(p.page_ptr))[t.node] : 0;
     // Contiguous: K/V at the piece's first token; paged and flattened: the
     // head's pool start (blocks add their rows), or for a flattened chunk
     // over consecutive rows its first row.
@@ -1406,7 +1453,7 @@ void pac_kernel(PacParams p) {
     t.vbase = static_cast<const char*>(p.v) + off;
     bool done = false, finished = true;
     if constexpr (sizeof(T) == 2) {
-      if (t.row_count >= p.mfma_min_rows) {
+      if (!DOT || t.row_count >= p.mfma_min_rows) {
         // Slabs of 16 RBR rows, TS wavefronts per slab.
         static_assert(NW == 8, "row dispatch for 8 wavefronts");
         // Bandwidth-bound layouts stream K/V with the non-temporal hint
@@ -1430,7 +1477,9 @@ void pac_kernel(PacParams p) {
         done = true;
       }
     }
-    if (!done) dot_piece<T, D, NW>(p, t, kvh);
+    if constexpr (DOT) {
+      if (!done) dot_piece<T, D, NW>(p, t, kvh);
+    }
     __syncthreads();  // the piece is finished with the LDS (and with task_lds)
     retry = !finished;
     if (finished) {
@@ -1441,7 +1490,7 @@ void pac_kernel(PacParams p) {
   }
 }
 
-template <typename T, int D, int LAYOUT>
+template <typename T, int D, int LAYOUT, bool DOT>
 int launch_layout(const PacParams& p, void* stream) {
   const int grid = p.num_bins * p.hkv;
   constexpr size_t lds = LAYOUT == kFlat ? kLdsBytesFlat : kLdsBytes;
@@ -1453,19 +1502,26 @@ int launch_layout(const PacParams& p, void* stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return static_cast<int>(e);
   if (dev < 0 || dev >= kMaxDevices || !configured[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pac_kernel<T, D, LAYOUT>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pac_kernel<T, D, LAYOUT, DOT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return static_cast<int>(e);
     if (dev >= 0 && dev < kMaxDevices) configured[dev] = true;
   }
-  hipLaunchKernelGGL((pac_kernel<T, D, LAYOUT>), dim3(grid), dim3(kWaves<T> * 64), lds,
+  hipLaunchKernelGGL((pac_kernel<T, D, LAYOUT, DOT>), dim3(grid), dim3(kWaves<T> * 64), lds,
                      static_cast<hipStream_t>(stream), p);
   return static_cast<int>(hipGetLastError());
 }
+template <typename T, int D, bool DOT>
+int launch_dot(const PacParams& p, void* stream) {
+  if (p.mask_words > 0) return launch_layout<T, D, kFlat, DOT>(p, stream);
+  return p.page_shift >= 0 ? launch_layout<T, D, kPaged, DOT>(p, stream) : launch_layout<T, D, kContig, DOT>(p, stream);
+}
 template <typename T, int D>
 int launch_one(const PacParams& p, void* stream) {
-  if (p.mask_words > 0) return launch_layout<T, D, kFlat>(p, stream);
-  return p.page_shift >= 0 ? launch_layout<T, D, kPaged>(p, stream) : launch_layout<T, D, kContig>(p, stream);
+  if constexpr (sizeof(T) == 2) {
+    if (p.mfma_min_rows <= 1) return launch_dot<T, D, false>(p, stream);
+  }
+  return launch_dot<T, D, true>(p, stream);
 }
 
 }  // namespace
@@ -1481,13 +1537,13 @@ int launch_pac(const PacParams& p, int in_dtype, int head_dim, void* stream) {
 int pac_blocks_per_cu(int in_dtype, int head_dim, int* blocks) {
   hipError_t e;
   if (in_dtype == PST_BF16 && head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 128, kContig>, kWaves<uint16_t> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 128, kContig, false>, kWaves<uint16_t> * 64, kLdsBytes);
   else if (in_dtype == PST_BF16)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 64, kContig>, kWaves<uint16_t> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 64, kContig, false>, kWaves<uint16_t> * 64, kLdsBytes);
   else if (head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 128, kContig>, kWaves<float> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 128, kContig, true>, kWaves<float> * 64, kLdsBytes);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 64, kContig>, kWaves<float> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 64, kContig, true>, kWaves<float> * 64, kLdsBytes);
   return static_cast<int>(e);
 }
 
