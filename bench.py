@@ -8,8 +8,12 @@ the plan built before the timed region and reused (plans are reused across
 decode steps and layers).  Before every step a 1 GiB read of a buffer that is
 never written evicts L2 and the last-level cache without leaving dirty lines
 behind, so every step reads its KV from HBM and pays for no write-back of
-the eviction; the kernels are timed with HIP events recorded on the stream
-they run on.  Prints one JSON line.
+the eviction.  A step is timed as one ``pst_decode_attn`` call (the library
+enqueues PAC and POR back to back) between two HIP events recorded on the
+stream it runs on; a second pass puts an event between the two kernels for
+the per-kernel split (``pac_ms``, ``por_ms``; the roofline uses ``pac_ms``).
+The output is in the input dtype, the library's default.  Prints one JSON
+line.
 """
 from __future__ import annotations
 
@@ -95,15 +99,27 @@ def evict(pst, bufs):
 
 
 def time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, steps, warmup):
-    """Per step: evict the caches, then PAC and POR bracketed by events on the current stream."""
+    """Cold steps on the current stream.  Pass 1: one ``pst_decode_attn``
+    call (PAC then POR, enqueued back to back by the library) between two
+    events: the step time.  Pass 2: events before PAC, between PAC and POR
+    and after POR: the per-kernel split (each event on the stream adds a few
+    microseconds, so the split sums to more than the step)."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         evict(pst, evict_bufs)
-        pst.pac(plan, q, k, v, ws)
-        pst.por(plan, out, lse, ws)
+        pst.decode_attn(plan, q, k, v, out=out, lse=lse, ws=ws)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     t0 = time.perf_counter()
+    for i in range(steps):
+        evict(pst, evict_bufs)
+        ev[i][0].record(stream)
+        pst.decode_attn(plan, q, k, v, out=out, lse=lse, ws=ws)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for i in range(steps):
         evict(pst, evict_bufs)
         ev[i][0].record(stream)
@@ -112,21 +128,18 @@ def time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, steps, warmu
         pst.por(plan, out, lse, ws)
         ev[i][2].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     pac_ms = [e[0].elapsed_time(e[1]) for e in ev]
     por_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    return pac_ms, por_ms, wall
+    return step_ms, pac_ms, por_ms, wall
 
 
 def time_warm(torch, pst, plan, q, k, v, out, lse, ws, steps):
     stream = torch.cuda.current_stream()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    pst.pac(plan, q, k, v, ws)
-    pst.por(plan, out, lse, ws)
+    pst.decode_attn(plan, q, k, v, out=out, lse=lse, ws=ws)
     a.record(stream)
     for _ in range(steps):
-        pst.pac(plan, q, k, v, ws)
-        pst.por(plan, out, lse, ws)
+        pst.decode_attn(plan, q, k, v, out=out, lse=lse, ws=ws)
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
@@ -185,9 +198,9 @@ def shape_sweep(torch, pst, workloads, a):
     for spec in shapes:
         print(f"[bench] shape {spec.name}", file=sys.stderr, flush=True)
         q, k, v = workloads.make_tensors(spec, "cuda")
-        tree = pst.Tree.from_spec(spec, out_dtype="f32")
+        tree = pst.Tree.from_spec(spec)
         st = workload_stats(spec, tree)
-        out = torch.empty((spec.num_queries, spec.num_q_heads, spec.head_dim), device="cuda", dtype=torch.float32)
+        out = torch.empty((spec.num_queries, spec.num_q_heads, spec.head_dim), device="cuda", dtype=q.dtype)
         lse = torch.empty((spec.num_queries, spec.num_q_heads), device="cuda", dtype=torch.float32)
         r = {"nodes": spec.num_nodes, "queries": spec.num_queries, "unique_kv_bytes": st["unique_kv_bytes"],
              "per_query_kv_bytes": st["per_query_kv_bytes"],
@@ -195,8 +208,8 @@ def shape_sweep(torch, pst, workloads, a):
         for name, kw in (("tree", {}), ("tree_no_split", {"no_split": True}), ("query_guided", {"query_guided": True})):
             plan = pst.Plan(tree, **kw)
             ws = pst.workspace(plan)
-            pac, por, _ = time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, a.steps, a.warmup)
-            r[name + "_ms"] = statistics.mean(x + y for x, y in zip(pac, por))
+            steps, _, _, _ = time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, a.steps, a.warmup)
+            r[name + "_ms"] = statistics.mean(steps)
             del ws, plan
         r["speedup_over_query_guided"] = r["query_guided_ms"] / r["tree_ms"]
         r["speedup_of_partitioning"] = r["tree_no_split_ms"] / r["tree_ms"]
@@ -227,9 +240,9 @@ def flatten_sweep(torch, pst, workloads, a):
     for spec in specs:
         print(f"[bench] partitions of {spec.name}", file=sys.stderr, flush=True)
         q, k, v = workloads.make_tensors(spec, "cuda")
-        tree = pst.Tree.from_spec(spec, out_dtype="f32")
+        tree = pst.Tree.from_spec(spec)
         st = workload_stats(spec, tree)
-        out = torch.empty((spec.num_queries, spec.num_q_heads, spec.head_dim), device="cuda", dtype=torch.float32)
+        out = torch.empty((spec.num_queries, spec.num_q_heads, spec.head_dim), device="cuda", dtype=q.dtype)
         lse = torch.empty((spec.num_queries, spec.num_q_heads), device="cuda", dtype=torch.float32)
         variants = [("cost_model", {}), ("node", {"no_split": True})]
         variants += [(f"node_chunk_{c}", {"fixed_chunk": c}) for c in chunks]
@@ -245,8 +258,8 @@ def flatten_sweep(torch, pst, workloads, a):
         for name, kw in variants:
             plan = pst.Plan(tree, **kw)
             ws = pst.workspace(plan)
-            pac, por, _ = time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, a.steps, a.warmup)
-            r[name + "_ms"] = statistics.mean(x + y for x, y in zip(pac, por))
+            steps, _, _, _ = time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, a.steps, a.warmup)
+            r[name + "_ms"] = statistics.mean(steps)
             r[name + "_tasks"] = int(len(plan.view()["tasks"]))
             del ws, plan
         best = min((c for c in chunks), key=lambda c: r[f"flatten_{c}_ms"])
@@ -374,21 +387,21 @@ def main():
         paged, kk, vv = workloads.page_pools(spec, k, v, a.page_size, fill=0.0,
                                              scatter=a.page_order == "scattered")
     t0 = time.perf_counter()
-    tree = pst.Tree.from_paged(spec, paged, out_dtype="f32") if paged else pst.Tree.from_spec(spec, out_dtype="f32")
+    tree = pst.Tree.from_paged(spec, paged) if paged else pst.Tree.from_spec(spec)
     t_tree = (time.perf_counter() - t0) * 1e3
     t0 = time.perf_counter()
     plan = pst.Plan(tree, flatten=a.flatten) if a.flatten else pst.Plan(tree)
     t_plan = (time.perf_counter() - t0) * 1e3
     st = workload_stats(spec, tree)
     pv = plan.view()
-    out = torch.empty((spec.num_queries, spec.num_q_heads, spec.head_dim), device="cuda", dtype=torch.float32)
+    out = torch.empty((spec.num_queries, spec.num_q_heads, spec.head_dim), device="cuda", dtype=q.dtype)
     lse = torch.empty((spec.num_queries, spec.num_q_heads), device="cuda", dtype=torch.float32)
     ws = pst.workspace(plan)
     evict_bufs = (torch.empty(1 << 30, dtype=torch.uint8, device="cuda"), torch.empty(4096, dtype=torch.float32, device="cuda"))
 
     print(f"[bench] timing {a.steps} cold steps", file=sys.stderr, flush=True)
-    pac_ms, por_ms, wall = time_steps(torch, pst, plan, q, kk, vv, out, lse, ws, evict_bufs, a.steps, a.warmup)
-    step_ms = [x + y for x, y in zip(pac_ms, por_ms)]
+    step_ms, pac_ms, por_ms, wall = time_steps(torch, pst, plan, q, kk, vv, out, lse, ws, evict_bufs, a.steps,
+                                               a.warmup)
     ms = statistics.mean(step_ms)
     pac_avg = statistics.mean(pac_ms)
     warm_ms = None if a.no_warm else time_warm(torch, pst, plan, q, kk, vv, out, lse, ws, a.steps)
@@ -513,14 +526,14 @@ def gate(torch, pst, workloads, evict_bufs, a):
         spec = workloads.config(name)
         print(f"[bench] gate workload {spec.name}", file=sys.stderr, flush=True)
         q, k, v = workloads.make_tensors(spec, "cuda")
-        tree = pst.Tree.from_spec(spec, out_dtype="f32")
+        tree = pst.Tree.from_spec(spec)
         plan = pst.Plan(tree)
         st = workload_stats(spec, tree)
-        out = torch.empty((spec.num_queries, spec.num_q_heads, spec.head_dim), device="cuda", dtype=torch.float32)
+        out = torch.empty((spec.num_queries, spec.num_q_heads, spec.head_dim), device="cuda", dtype=q.dtype)
         lse = torch.empty((spec.num_queries, spec.num_q_heads), device="cuda", dtype=torch.float32)
         ws = pst.workspace(plan)
-        pac, por, _ = time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, a.steps, a.gate_warmup)
-        ms = statistics.mean(x + y for x, y in zip(pac, por))
+        steps, pac, por, _ = time_steps(torch, pst, plan, q, k, v, out, lse, ws, evict_bufs, a.steps, a.gate_warmup)
+        ms = statistics.mean(steps)
         rows[spec.name] = {
             "config": name, "ms_per_step": ms, "pac_ms": statistics.mean(pac), "por_ms": statistics.mean(por),
             "unique_kv_bytes": st["unique_kv_bytes"], "logical_tokens": st["logical_tokens"],
