@@ -290,8 +290,13 @@ pst_status pst_plan(pst_tree_t tree, pst_cost_model_t cost, const pst_plan_opts*
  * PST_E_UNSUPPORTED when a kv head's K/V span more than 2^31 - 1 bytes. */
 
 /* Bytes of device workspace pst_decode_attn needs: the partial outputs
- * [num_slots][num_q_heads][head_dim] float32 plus their LSE
- * [num_slots][num_q_heads] float32, 256-byte aligned. */
+ * [num_slots][num_q_heads][head_dim] plus their LSE [num_slots][num_q_heads],
+ * each 256-byte aligned.  The partials are float32 with float32 LSE, except
+ * when the tree's input and output are both bf16 and every piece of the plan
+ * runs on the matrix cores (no PST_PLAN_DOT_SMALL): then each partial is
+ * float16, scaled by a power of two 2^(15 - e) chosen from its piece's V,
+ * and each LSE is an (LSE float32, e int32) pair.  The fp16 rounding
+ * (2^-11 relative) is a quarter of the bf16 output's own. */
 pst_status pst_plan_workspace_size(pst_plan_t plan, size_t* bytes);
 
 /* Host views of a plan (bit-exact comparisons, introspection). */

@@ -848,11 +848,25 @@ pst_status pst_plan(pst_tree_t t, pst_cost_model_t cost, const pst_plan_opts* op
 
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Partial outputs in fp16 (with a power-of-two scale per slot and head)
+// when the output is bf16 anyway and every piece runs on the matrix cores
+// (bf16 input, no dot-product pieces): half the bytes PAC writes and POR
+// reads, at a rounding (2^-11 relative) four times finer than the bf16
+// output's own.  float32 otherwise.
+static bool partials_f16(const pst_plan_s* p) {
+  const pst_shape& s = p->tree->shape;
+  return s.in_dtype == PST_BF16 && s.out_dtype == PST_BF16 && p->opts.mfma_min_rows <= 1;
+}
+
+// Workspace: partial outputs [slots][hq][d], then their LSE [slots][hq]
+// (float32; for fp16 partials, (LSE, scale exponent) pairs of 8 bytes), each
+// array 256-byte aligned.
 static void workspace_layout(const pst_plan_s* p, size_t* o_bytes, size_t* total) {
   const pst_shape& s = p->tree->shape;
   const size_t slots = p->r.slot_ptr.empty() ? 0 : static_cast<size_t>(p->r.slot_ptr.back());
-  *o_bytes = align256(slots * s.num_q_heads * s.head_dim * sizeof(float));
-  *total = *o_bytes + align256(slots * s.num_q_heads * sizeof(float));
+  const bool f16 = partials_f16(p);
+  *o_bytes = align256(slots * s.num_q_heads * s.head_dim * (f16 ? 2 : sizeof(float)));
+  *total = *o_bytes + align256(slots * s.num_q_heads * (f16 ? 2 : 1) * sizeof(float));
 }
 
 pst_status pst_plan_workspace_size(pst_plan_t p, size_t* bytes) {
@@ -933,6 +947,7 @@ pst_status pst_pac(pst_plan_t p, const void* q, const void* k, const void* v, vo
   pp.v = v;
   pp.opart = static_cast<float*>(ws);
   pp.lsepart = reinterpret_cast<float*>(static_cast<char*>(ws) + ob);
+  pp.part_f16 = partials_f16(p) ? 1 : 0;
   pp.tasks = p->d_tasks;
   pp.bin_ptr = p->d_bin_ptr;
   pp.nq_idx = t->d_nq_idx;
@@ -983,6 +998,7 @@ pst_status pst_por(pst_plan_t p, void* out, float* lse_out, const void* ws, size
   PorParams pp{};
   pp.opart = static_cast<const float*>(ws);
   pp.lsepart = reinterpret_cast<const float*>(static_cast<const char*>(ws) + ob);
+  pp.part_f16 = partials_f16(p) ? 1 : 0;
   pp.slot_ptr = p->d_slot_ptr;
   pp.out = out;
   pp.lse_out = lse_out;

@@ -336,14 +336,24 @@ __device__ __forceinline__ bool row_target(const PacParams& p, const TaskInfo& t
   return true;
 }
 
+__device__ __forceinline__ uint32_t pack_f16(float a, float b);
 // `slot` = first partial slot of the row's (query, node) entry (prefetched);
-// the piece's slot is slot + piece.
+// the piece's slot is slot + piece.  float32 partials: vals4 is the partial
+// output.  fp16 partials (part_f16): vals4 is the partial output times
+// 2^(15 - ev), below 2^16 in magnitude, rounded to nearest fp16; ev goes
+// beside the LSE (one 8-byte pair).
 __device__ __forceinline__ void write_partial(const PacParams& p, const TaskInfo& t, int slot0, int head, int D,
-                                              int d0, const float* vals4, float lse, bool write_lse) {
+                                              int d0, const float* vals4, float lse, bool write_lse, int ev) {
   const int64_t slot = static_cast<int64_t>(slot0) + t.piece;
-  float* dst = p.opart + (slot * p.hq + head) * D + d0;
-  *reinterpret_cast<float4*>(dst) = make_float4(vals4[0], vals4[1], vals4[2], vals4[3]);
-  if (write_lse) p.lsepart[slot * p.hq + head] = lse;
+  const int64_t at = (slot * p.hq + head) * D + d0;
+  if (p.part_f16) {
+    *reinterpret_cast<uint2*>(reinterpret_cast<_Float16*>(p.opart) + at) =
+        make_uint2(pack_f16(vals4[0], vals4[1]), pack_f16(vals4[2], vals4[3]));
+    if (write_lse) reinterpret_cast<float2*>(p.lsepart)[slot * p.hq + head] = make_float2(lse, __int_as_float(ev));
+  } else {
+    *reinterpret_cast<float4*>(p.opart + at) = make_float4(vals4[0], vals4[1], vals4[2], vals4[3]);
+    if (write_lse) p.lsepart[slot * p.hq + head] = lse;
+  }
 }
 
 // Flattened chunk: pool rows of N consecutive tokens from token `tok` of the
@@ -1091,12 +1101,13 @@ __device__ __forceinline__ bool mfma_piece(const PacParams& p, const TaskInfo& t
 #pragma unroll
     for (int rb = 0; rb < RBR; ++rb) {
       if (!qok[rb]) continue;
-      const float inv = l[rb] > 0.f ? exp2i(ev - 15) / l[rb] : 0.f;  // O carries the 2^(15 - ev) of V
+      // O carries the 2^(15 - ev) of V; fp16 partials keep it (ev goes with them).
+      const float inv = l[rb] > 0.f ? (p.part_f16 ? 1.f : exp2i(ev - 15)) / l[rb] : 0.f;
       const float lse = l[rb] > 0.f ? (m[rb] + __log2f(l[rb])) * kLn2 : kNegInf;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const float v4[4] = {o[db][rb][0] * inv, o[db][rb][1] * inv, o[db][rb][2] * inv, o[db][rb][3] * inv};
-        write_partial(p, t, slot0[rb], qhead[rb], D, db * 16 + lg * 4, v4, lse, db == 0 && lg == 0);
+        write_partial(p, t, slot0[rb], qhead[rb], D, db * 16 + lg * 4, v4, lse, db == 0 && lg == 0, ev);
       }
     }
   }
@@ -1349,7 +1360,7 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse = lt > 0.f ? (mm + __log2f(lt)) * kLn2 : kNegInf;
     const float v4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-    write_partial(p, t, out_slot[k], out_head[k], D, c4 * 4, v4, lse, c4 == 0);
+    write_partial(p, t, out_slot[k], out_head[k], D, c4 * 4, v4, lse, c4 == 0, 15);
   }
 }
 

@@ -37,7 +37,9 @@ constexpr float kNegInf = -__builtin_inff();
 // unused entries are not loaded and get weight 0.  The slot range is
 // uniform over the workgroup, so these choices are scalar branches.
 constexpr int kBatch = 8;
-template <int D, bool BF16_OUT>
+// F16: the partials are fp16 values times 2^(15 - e), with e per (slot, head)
+// in the (LSE, e) pair that replaces the LSE.
+template <int D, bool BF16_OUT, bool F16>
 __global__ __launch_bounds__(kPorThreads) void por_kernel(PorParams p, int chunks) {
   const int r = blockIdx.x / chunks;
   const int chunk = blockIdx.x % chunks;
@@ -58,8 +60,20 @@ __global__ __launch_bounds__(kPorThreads) void por_kernel(PorParams p, int chunk
       lse[j] = kNegInf;
       x[j] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (j < n) {
-        lse[j] = p.lsepart[(s + j) * p.hq + h];
-        x[j] = *reinterpret_cast<const float4*>(p.opart + ((s + j) * p.hq + h) * D + c4 * 4);
+        const int64_t at = ((s + j) * p.hq + h) * D + c4 * 4;
+        if constexpr (F16) {
+          typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+          const float2 le = reinterpret_cast<const float2*>(p.lsepart)[(s + j) * p.hq + h];
+          const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const _Float16*>(p.opart) + at);
+          lse[j] = le.x;
+          const float sc = __uint_as_float(static_cast<uint32_t>(__float_as_int(le.y) - 15 + 127) << 23);
+          const h2 a = __builtin_bit_cast(h2, u.x), b = __builtin_bit_cast(h2, u.y);
+          x[j] = make_float4(static_cast<float>(a[0]) * sc, static_cast<float>(a[1]) * sc,
+                             static_cast<float>(b[0]) * sc, static_cast<float>(b[1]) * sc);
+        } else {
+          lse[j] = p.lsepart[(s + j) * p.hq + h];
+          x[j] = *reinterpret_cast<const float4*>(p.opart + at);
+        }
       }
     }
     float bm = lse[0];
@@ -148,16 +162,22 @@ int launch_por(const PorParams& p, int head_dim, int out_dtype, void* stream) {
   const int chunks = (p.hq * (head_dim / 4) + kPorThreads - 1) / kPorThreads;
   const dim3 grid(static_cast<unsigned>(p.num_queries) * chunks), block(kPorThreads);
   const bool bf = out_dtype == PST_BF16;
-  if (head_dim == 128) {
-    if (bf)
-      hipLaunchKernelGGL((por_kernel<128, true>), grid, block, 0, s, p, chunks);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, p, chunks); };
+  if (p.part_f16) {  // bf16 output only
+    if (head_dim == 128)
+      go(por_kernel<128, true, true>);
     else
-      hipLaunchKernelGGL((por_kernel<128, false>), grid, block, 0, s, p, chunks);
+      go(por_kernel<64, true, true>);
+  } else if (head_dim == 128) {
+    if (bf)
+      go(por_kernel<128, true, false>);
+    else
+      go(por_kernel<128, false, false>);
   } else {
     if (bf)
-      hipLaunchKernelGGL((por_kernel<64, true>), grid, block, 0, s, p, chunks);
+      go(por_kernel<64, true, false>);
     else
-      hipLaunchKernelGGL((por_kernel<64, false>), grid, block, 0, s, p, chunks);
+      go(por_kernel<64, false, false>);
   }
   return static_cast<int>(hipGetLastError());
 }

@@ -123,8 +123,10 @@ struct PacParams {
   const void* q;
   const void* k;
   const void* v;
-  float* opart;    // [slots][hq][d]
-  float* lsepart;  // [slots][hq]
+  float* opart;    // [slots][hq][d] float32, or float16 when part_f16 (see below)
+  float* lsepart;  // [slots][hq] LSE; part_f16: [slots][hq] pairs (LSE, exponent e as int32 bits),
+                   // the fp16 partial being the output times 2^(15 - e)
+  int32_t part_f16;  // partials in fp16 with a per-(slot, head) power-of-two scale (bf16 in and out, matrix cores)
   const DevTask* tasks;
   const int32_t* bin_ptr;
   const int32_t* nq_idx;
@@ -148,8 +150,9 @@ struct PacParams {
 };
 
 struct PorParams {
-  const float* opart;
-  const float* lsepart;
+  const float* opart;     // float32, or float16 when part_f16
+  const float* lsepart;   // LSE, or (LSE, scale exponent) pairs when part_f16
+  int32_t part_f16;
   const int64_t* slot_ptr;
   void* out;
   float* lse_out;

@@ -56,8 +56,20 @@ def check(spec, tensors, out, lse, queries=None, tol=None, lse_tol=None, by_node
     got = out[queries].double().cpu().numpy()
     tol = TOL[spec.dtype] if tol is None else tol
     lse_tol = max(tol, 1e-5) * 4 if lse_tol is None else lse_tol
-    err = np.abs(got - O).max() if len(queries) else 0.0
     lerr = np.abs(lse[queries].double().cpu().numpy() - L).max() if len(queries) else 0.0
+    if out.dtype == torch.bfloat16:
+        # A bf16 output is the rounding to nearest of a value within `tol`:
+        # allow one bf16 ulp of the oracle's value on top (bf16 keeps 8
+        # significant bits).
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(O), 1e-38))) - 7)
+        excess = (np.abs(got - O) - ulp).max() if len(queries) else 0.0
+        err = np.abs(got - O).max() if len(queries) else 0.0
+        say(f"  {spec.name}: bf16 out, max|dO| = {err:.3e} (beyond one ulp {excess:.3e}), "
+            f"max|dLSE| = {lerr:.3e} over {len(queries)} queries")
+        assert excess <= tol, excess
+        assert lerr <= lse_tol, lerr
+        return err
+    err = np.abs(got - O).max() if len(queries) else 0.0
     say(f"  {spec.name}: max|dO| = {err:.3e}, max|dLSE| = {lerr:.3e} over {len(queries)} queries")
     assert err <= tol, err
     assert lerr <= lse_tol, lerr
@@ -134,11 +146,13 @@ def test_config_full(name):
     check(spec, t, out, lse)
 
 
-def test_config2_all_queries():
-    """The document-QA tree, every query (every head): the root's pieces and every leaf."""
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_config2_all_queries(out_dtype):
+    """The document-QA tree, every query (every head): the root's pieces and
+    every leaf; with a bf16 output the partials travel in fp16."""
     spec = workloads.config("2")
-    say(f"config 2: {spec.name}")
-    t, plan, out, lse = run(spec)
+    say(f"config 2: {spec.name}, {out_dtype} output")
+    t, plan, out, lse = run(spec, out_dtype=out_dtype)
     check(spec, t, out, lse, by_node=True)
 
 
@@ -155,10 +169,11 @@ def config4_queries(spec, extra=32, seed=1):
     return sorted(chosen)
 
 
-def test_config4_every_request():
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_config4_every_request(out_dtype):
     spec = workloads.config("4")
-    say(f"config 4: {spec.name}")
-    t, plan, out, lse = run(spec)
+    say(f"config 4: {spec.name}, {out_dtype} output")
+    t, plan, out, lse = run(spec, out_dtype=out_dtype)
     queries = config4_queries(spec)
     assert len({int(spec.parent[int(spec.query_node[r])]) for r in queries}) == 16
     check(spec, t, out, lse, queries=queries)
@@ -490,12 +505,14 @@ def test_random_configurations(seed):
                                  masked_prob=float(rng.choice([0.0, 0.3])))
     q, k, v = workloads.make_tensors(spec, "cuda")
     P = int(rng.choice([0, 0, 8, 16, 64, 128, 256, 512]))
+    # The output dtype from a generator of its own (the other draws stay as they were).
+    odt = "bf16" if dtype == "bf16" and np.random.default_rng(20000 + seed).random() < 0.5 else "f32"
     if P:
         paged, kk, vv = workloads.page_pools(spec, k, v, P, spare_pages=int(rng.integers(0, 2)))
-        tree = pst.Tree.from_paged(spec, paged, out_dtype="f32")
+        tree = pst.Tree.from_paged(spec, paged, out_dtype=odt)
     else:
         kk, vv = k, v
-        tree = pst.Tree.from_spec(spec, out_dtype="f32")
+        tree = pst.Tree.from_spec(spec, out_dtype=odt)
     kw = dict(num_bins=int(rng.choice([0, 1, 3, 7, 32])), dot_small=bool(rng.random() < 0.3))
     if dtype == "bf16" and g <= 32 and rng.random() < 0.25:
         kw["max_rows"] = int(rng.choice([32, 64, 128]))
@@ -506,7 +523,7 @@ def test_random_configurations(seed):
         kw["flatten"] = int(rng.choice([128, 256, 384, 640]))
     elif u < 0.55:
         kw["no_split"] = True
-    say(f"seed {seed}: {dtype} H {hkv * g}/{hkv} d {d} N {spec.num_nodes} B {spec.num_queries} page {P} {kw}")
+    say(f"seed {seed}: {dtype} (out {odt}) H {hkv * g}/{hkv} d {d} N {spec.num_nodes} B {spec.num_queries} page {P} {kw}")
     plan = pst.Plan(tree, **kw)
     out, lse = pst.decode_attn(plan, q, kk, vv)
     torch.cuda.synchronize()
@@ -524,12 +541,65 @@ def test_max_rows_split():
 
 
 def test_bf16_output_rounding():
+    """bf16 output: every query against the oracle (one bf16 ulp beyond the
+    tolerance), and within one ulp plus the fp16 partials' rounding (2^-11
+    of the largest partial, bounded by max|V|) of the float32-output run."""
     spec = workloads.config("3")
-    t, plan, out_bf, _ = run(spec, out_dtype="bf16")
+    t, plan, out_bf, lse_bf = run(spec, out_dtype="bf16")
     _, _, out32, lse32 = run(spec, tensors=t)
     assert out_bf.dtype == torch.bfloat16
-    # POR rounds its float32 result to nearest even: identical to rounding the float32 output.
-    assert torch.equal(out_bf, out32.to(torch.bfloat16))
+    check(spec, t, out_bf, lse_bf)
+    vmax = float(t[2].float().abs().max())
+    ulp = torch.exp2(torch.floor(torch.log2(out32.abs().clamp_min(1e-38))) - 7)
+    assert ((out_bf.float() - out32).abs() - ulp).max().item() <= 2.0 ** -10 * vmax
+    assert torch.equal(lse_bf, lse32) or (lse_bf - lse32).abs().max().item() <= 1e-5
+
+
+# Two nodes per query whose V differ in scale by 2^(2 s): the partials of one
+# query carry different fp16 scales into the merge.
+@pytest.mark.parametrize("s", [6, 20])
+def test_bf16_output_mixed_scales(s):
+    """bf16 output, partials in fp16 with their own power-of-two scale: a
+    root whose V is scaled by 2^s and leaves scaled by 2^-s, peaked queries
+    (q x 8), so every query merges partials of very different magnitude.
+    Each (query, head) is held to a tolerance weighted by how much each node
+    contributes (its merge weight from the float64 partials), so a wrong
+    scale on either partial shows."""
+    lens = [1500] + [300] * 6
+    spec = workloads.TreeSpec(f"mixed{s}", np.array([-1] + [0] * 6), np.array(lens),
+                              np.concatenate([[0], np.cumsum(lens)[:-1]]), np.repeat(np.arange(1, 7), 3),
+                              16, 2, 128, "bf16", 91)
+    q, k, v = workloads.make_tensors(spec, "cuda", q_scale=8.0)
+    f = torch.full((spec.total_tokens,), 2.0 ** -s, device="cuda")
+    f[:1500] = 2.0 ** s
+    v = (v.float() * f[None, :, None]).to(torch.bfloat16).contiguous()
+    t, plan, out, lse = run(spec, out_dtype="bf16", tensors=(q, k, v), num_bins=5)
+    _, _, out32, _ = run(spec, tensors=(q, k, v), num_bins=5)
+    assert plan.view()["num_slots"] > spec.num_queries  # merges happen
+    O, _ = oracle.attend(spec, q, k, v)
+    qh, kh, vh = (x.double().cpu().numpy() for x in (q, k, v))
+    g = spec.num_q_heads // spec.num_kv_heads
+    scale = 1.0 / math.sqrt(spec.head_dim)
+    vmax = np.abs(vh).max(axis=2)  # [H_kv, T]
+    bound = np.zeros((spec.num_queries, spec.num_q_heads))
+    for r, n in enumerate(spec.query_node):
+        lo, hi = int(spec.kv_offset[n]), int(spec.kv_offset[n] + spec.kv_len[n])
+        for h in range(spec.num_q_heads):
+            kv = h // g
+            parts = [(0, 1500), (lo, hi)]
+            lses = [oracle.partial_attend(qh[r, h][None], kh[kv, a:b], vh[kv, a:b], scale)[3][0] for a, b in parts]
+            top = max(lses)
+            w = np.exp(np.array(lses) - top)
+            w /= w.sum()
+            bound[r, h] = sum(wi * vmax[kv, a:b].max() for wi, (a, b) in zip(w, parts))
+    got = out.double().cpu().numpy()
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(O), 1e-38))) - 7)
+    excess = (np.abs(got - O) - ulp - TOL["bf16"] * bound[:, :, None]).max()
+    say(f"  mixed scales 2^+-{s}: largest excess over the weighted bound {excess:.3e}")
+    assert excess <= 0.0
+    o32 = out32.double().cpu().numpy()
+    ulp32 = np.exp2(np.floor(np.log2(np.maximum(np.abs(o32), 1e-38))) - 7)
+    assert (np.abs(got - o32) - ulp32 - 2.0 ** -10 * bound[:, :, None]).max() <= 0.0
 
 
 def test_query_guided_baseline():
@@ -616,11 +686,13 @@ VSCALE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("rows,vscale,ramp", VSCALE_CASES)
-def test_v_magnitudes(rows, vscale, ramp):
+def test_v_magnitudes(rows, vscale, ramp, out_dtype):
     """V far from unit scale, under peaked attention (q x 8), on one
     1000-token node of `rows` MQA rows (every matrix-core layout): the
-    max-abs error stays within the bf16 tolerance relative to max|V|."""
+    max-abs error stays within the bf16 tolerance relative to max|V|; with a
+    bf16 output the fp16 partial carries the piece's scale to the merge."""
     spec = workloads.TreeSpec(f"vscale{rows}", np.array([-1]), np.array([1000]), np.array([0]), np.array([0]),
                               rows, 1, 128, "bf16", 83)
     q, k, v = workloads.make_tensors(spec, "cuda", q_scale=8.0)
@@ -630,7 +702,7 @@ def test_v_magnitudes(rows, vscale, ramp):
     v = (v.float() * f[None, :, None]).to(torch.bfloat16).contiguous()
     vmax = float(v.float().abs().max())
     say(f"rows {rows}, V x {vscale:g}, ramp {ramp}, max|V| {vmax:.3e}")
-    t, plan, out, lse = run(spec, tensors=(q, k, v), num_bins=1)
+    t, plan, out, lse = run(spec, tensors=(q, k, v), num_bins=1, out_dtype=out_dtype)
     assert plan.view()["b_eff"][0] == 1  # one piece: every raise of the scale happens inside it
     check(spec, t, out, lse, tol=TOL["bf16"] * vmax, lse_tol=4 * TOL["bf16"])
 
