@@ -1369,11 +1369,15 @@ __device__ __forceinline__ void dot_piece(const PacParams& p, const TaskInfo& t,
 // scalar registers stay with the tile loop).  DOT: the kernel holds the
 // dot-product path (float inputs; bf16 plans that send small pieces there).
 // The bf16 kernels of the other plans leave it out: its code, inlined
-// beside the matrix-core loops, costs them registers and schedule.
-template <typename T, int D, int LAYOUT, bool DOT>
+// beside the matrix-core loops, costs them registers and schedule.  F16: the
+// partials are written in fp16 (PacParams::part_f16), fixed per kernel so
+// the other format's stores compile away (as a run-time flag it cost the
+// contiguous kernel scalar-register spills).
+template <typename T, int D, int LAYOUT, bool DOT, bool F16>
 __global__ __launch_bounds__(kWaves<T> * 64) __attribute__((amdgpu_waves_per_eu(kWaves<T> / 4, kWaves<T> / 4)))
 void pac_kernel(PacParams p) {
   constexpr int NW = kWaves<T>;
+  p.part_f16 = F16 ? 1 : 0;
   if constexpr (LAYOUT != kPaged)
     p.page_shift = -1;  // every page-table branch folds away
   else
@@ -1472,7 +1476,7 @@ void pac_kernel(PacParams p) {
   }
 }
 
-template <typename T, int D, int LAYOUT, bool DOT>
+template <typename T, int D, int LAYOUT, bool DOT, bool F16>
 int launch_layout(const PacParams& p, void* stream) {
   const int grid = p.num_bins * p.hkv;
   constexpr size_t lds = LAYOUT == kFlat ? kLdsBytesFlat : kLdsBytes;
@@ -1484,26 +1488,31 @@ int launch_layout(const PacParams& p, void* stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return static_cast<int>(e);
   if (dev < 0 || dev >= kMaxDevices || !configured[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pac_kernel<T, D, LAYOUT, DOT>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pac_kernel<T, D, LAYOUT, DOT, F16>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return static_cast<int>(e);
     if (dev >= 0 && dev < kMaxDevices) configured[dev] = true;
   }
-  hipLaunchKernelGGL((pac_kernel<T, D, LAYOUT, DOT>), dim3(grid), dim3(kWaves<T> * 64), lds,
+  hipLaunchKernelGGL((pac_kernel<T, D, LAYOUT, DOT, F16>), dim3(grid), dim3(kWaves<T> * 64), lds,
                      static_cast<hipStream_t>(stream), p);
   return static_cast<int>(hipGetLastError());
 }
-template <typename T, int D, bool DOT>
+template <typename T, int D, bool DOT, bool F16>
 int launch_dot(const PacParams& p, void* stream) {
-  if (p.mask_words > 0) return launch_layout<T, D, kFlat, DOT>(p, stream);
-  return p.page_shift >= 0 ? launch_layout<T, D, kPaged, DOT>(p, stream) : launch_layout<T, D, kContig, DOT>(p, stream);
+  if (p.mask_words > 0) return launch_layout<T, D, kFlat, DOT, F16>(p, stream);
+  return p.page_shift >= 0 ? launch_layout<T, D, kPaged, DOT, F16>(p, stream)
+                           : launch_layout<T, D, kContig, DOT, F16>(p, stream);
 }
+// fp16 partials only come with bf16 plans that run every piece on the
+// matrix cores (the kernels without the dot path).
 template <typename T, int D>
 int launch_one(const PacParams& p, void* stream) {
   if constexpr (sizeof(T) == 2) {
-    if (p.mfma_min_rows <= 1) return launch_dot<T, D, false>(p, stream);
+    if (p.mfma_min_rows <= 1)
+      return p.part_f16 ? launch_dot<T, D, false, true>(p, stream) : launch_dot<T, D, false, false>(p, stream);
   }
-  return launch_dot<T, D, true>(p, stream);
+  if (p.part_f16) return static_cast<int>(hipErrorInvalidValue);
+  return launch_dot<T, D, true, false>(p, stream);
 }
 
 }  // namespace
@@ -1519,13 +1528,13 @@ int launch_pac(const PacParams& p, int in_dtype, int head_dim, void* stream) {
 int pac_blocks_per_cu(int in_dtype, int head_dim, int* blocks) {
   hipError_t e;
   if (in_dtype == PST_BF16 && head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 128, kContig, false>, kWaves<uint16_t> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 128, kContig, false, true>, kWaves<uint16_t> * 64, kLdsBytes);
   else if (in_dtype == PST_BF16)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 64, kContig, false>, kWaves<uint16_t> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<uint16_t, 64, kContig, false, true>, kWaves<uint16_t> * 64, kLdsBytes);
   else if (head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 128, kContig, true>, kWaves<float> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 128, kContig, true, false>, kWaves<float> * 64, kLdsBytes);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 64, kContig, true>, kWaves<float> * 64, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, pac_kernel<float, 64, kContig, true, false>, kWaves<float> * 64, kLdsBytes);
   return static_cast<int>(e);
 }
 
