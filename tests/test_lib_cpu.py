@@ -158,6 +158,30 @@ def test_bad_plan_options():
     _raises("PST_E_UNSUPPORTED", pst.Plan, t, max_rows=64, host_only=True)  # float32 rows > 16
 
 
+def _a256(n):
+    return -(-n // 256) * 256
+
+
+@pytest.mark.parametrize("odt", ["f32", "bf16"])
+@pytest.mark.parametrize("dot_small", [False, True])
+def test_workspace_layout(odt, dot_small):
+    """The workspace holds the partial outputs and their LSE: float32 partials
+    and float32 LSE, or, when input and output are bf16 and every piece runs on
+    the matrix cores, fp16 partials and (LSE, exponent) pairs; each array
+    256-byte aligned (the layout include/pst.h states)."""
+    spec = workloads.config("3")
+    t = _tree(spec, out_dtype=odt)
+    plan = pst.Plan(t, num_bins=32, host_only=True, dot_small=dot_small)
+    S, H, D = plan.view()["num_slots"], spec.num_q_heads, spec.head_dim
+    f16 = odt == "bf16" and not dot_small
+    want = _a256(S * H * D * (2 if f16 else 4)) + _a256(S * H * (8 if f16 else 4))
+    assert plan.workspace_bytes == want
+    t32 = _tree(workloads.config("1"))
+    p32 = pst.Plan(t32, num_bins=4, host_only=True)
+    v = p32.view()
+    assert p32.workspace_bytes == _a256(v["num_slots"] * 4 * 64 * 4) + _a256(v["num_slots"] * 4 * 4)
+
+
 def test_engine_threshold():
     """bf16 plans put every piece on the matrix cores unless PST_PLAN_DOT_SMALL asks for the
     dot-product path below 16 rows; float32 plans never use them."""
