@@ -1041,6 +1041,33 @@ __device__ __forceinline__ bool mfma_piece(const PacParams& p, const TaskInfo& t
     x = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
     if (lane == 0) wave_vmax[w] = x;
   }
+  // Two wavefronts per slab hand half 1's state to half 0 through LDS.  With
+  // one row block per wavefront (at most 32 rows) that state fits the 16 KB
+  // above the tile stages, which no tile uses, so it is written before the
+  // barrier that ends the tiles and that one barrier publishes both; larger
+  // states reuse the tile stages after it.
+  constexpr bool kEarlyHandOff = TS == 2 && RBR == 1;
+  float* const so = reinterpret_cast<float*>(lds + (kEarlyHandOff ? kTileBytes : 0));  // [slab][rb][db][lane][4]
+  float* const sml = reinterpret_cast<float*>(lds + kAuxOff);                             // [slab][rb][lane][2]
+  auto hand_off = [&]() {
+    // Row sums first: the four lane groups hold different tokens of the same rows.
+#pragma unroll
+    for (int rb = 0; rb < RBR; ++rb) {
+      l[rb] += __shfl_xor(l[rb], 16);
+      l[rb] += __shfl_xor(l[rb], 32);
+    }
+    if (TS == 2 && active && half == 1) {
+#pragma unroll
+      for (int rb = 0; rb < RBR; ++rb) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          *reinterpret_cast<f32x4*>(so + (((slab * RBR + rb) * DB + db) * 64 + lane) * 4) = o[db][rb];
+        sml[((slab * RBR + rb) * 64 + lane) * 2 + 0] = m[rb];
+        sml[((slab * RBR + rb) * 64 + lane) * 2 + 1] = l[rb];
+      }
+    }
+  };
+  if constexpr (kEarlyHandOff) hand_off();
   __syncthreads();  // all wavefronts are done with the tiles: reuse the LDS
   {
     float pm = 0.f;
@@ -1058,27 +1085,10 @@ __device__ __forceinline__ bool mfma_piece(const PacParams& p, const TaskInfo& t
     if (retry) ev_carry = min(kEvMax, ev + 2);  // headroom for the next piece's larger values
   }
 
-  // Row sums: the four lane groups hold different tokens of the same rows.
-#pragma unroll
-  for (int rb = 0; rb < RBR; ++rb) {
-    l[rb] += __shfl_xor(l[rb], 16);
-    l[rb] += __shfl_xor(l[rb], 32);
-  }
+  if constexpr (!kEarlyHandOff) hand_off();
   if constexpr (TS == 2) {
-    // Merge the two token halves of every slab: half 1 hands its state to half 0.
-    float* so = reinterpret_cast<float*>(lds);              // [slab][rb][db][lane][4]
-    float* sml = reinterpret_cast<float*>(lds + kAuxOff);   // [slab][rb][lane][2]
-    if (active && half == 1) {
-#pragma unroll
-      for (int rb = 0; rb < RBR; ++rb) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          *reinterpret_cast<f32x4*>(so + (((slab * RBR + rb) * DB + db) * 64 + lane) * 4) = o[db][rb];
-        sml[((slab * RBR + rb) * 64 + lane) * 2 + 0] = m[rb];
-        sml[((slab * RBR + rb) * 64 + lane) * 2 + 1] = l[rb];
-      }
-    }
-    __syncthreads();
+    // Merge the two token halves of every slab: half 1 handed its state to half 0.
+    if constexpr (!kEarlyHandOff) __syncthreads();
     if (active && half == 0) {
 #pragma unroll
       for (int rb = 0; rb < RBR; ++rb) {
@@ -1396,18 +1406,23 @@ void pac_kernel(PacParams p) {
   const int64_t esz = sizeof(T);
   // The next piece's record travels one dword per lane (lanes 0..11 of every
   // wavefront) while the current piece runs, and is handed over through LDS.
+  // Two record slots: piece ti reads slot (ti - tb) & 1 and, before the
+  // barrier that ends it, wavefront 0 writes the next record into the other
+  // slot, which nobody reads any more, so that one barrier per piece orders
+  // both.
   constexpr int TW = sizeof(DevTask) / 4;
-  uint32_t* const task_lds = reinterpret_cast<uint32_t*>(pac_lds + kAuxOff + kAuxBytes - sizeof(DevTask));
+  uint32_t* const rec_lds = reinterpret_cast<uint32_t*>(pac_lds + kAuxOff + kAuxBytes - 2 * sizeof(DevTask));
   const int tid = static_cast<int>(__builtin_amdgcn_workitem_id_x());
-  if (tb < te && tid < TW) task_lds[tid] = reinterpret_cast<const uint32_t*>(p.tasks + tb)[tid];
+  if (tb < te && tid < TW) rec_lds[tid] = reinterpret_cast<const uint32_t*>(p.tasks + tb)[tid];
   __syncthreads();
   int ev_carry = kEvStart;  // the V scale exponent the next matrix-core piece starts from
-  bool retry = false;  // the task in task_lds runs again with the V scale its first pass found
+  bool retry = false;  // the current task runs again with the V scale its first pass found
   for (int ti = tb; ti < te;) {
+    const int slot = (ti - tb) & 1;
     DevTask task;
-    __builtin_memcpy(&task, task_lds, sizeof(DevTask));
+    __builtin_memcpy(&task, rec_lds + slot * TW, sizeof(DevTask));
     uint32_t next_word = 0;
-    if (ti + 1 < te && (tid & 63) < TW) next_word = reinterpret_cast<const uint32_t*>(p.tasks + ti + 1)[tid & 63];
+    if (ti + 1 < te && tid < TW) next_word = reinterpret_cast<const uint32_t*>(p.tasks + ti + 1)[tid];
     // The record is the same in every lane: read it as wave-uniform values so
     // that everything derived from it (trip counts, active wavefronts) is
     // scalar control flow and the barriers stay in uniform code.
@@ -1466,13 +1481,10 @@ void pac_kernel(PacParams p) {
     if constexpr (DOT) {
       if (!done) dot_piece<T, D, NW>(p, t, kvh);
     }
-    __syncthreads();  // the piece is finished with the LDS (and with task_lds)
+    if (tid < TW) rec_lds[(slot ^ 1) * TW + tid] = next_word;
+    __syncthreads();  // the piece is finished with the LDS; the next record is in place
     retry = !finished;
-    if (finished) {
-      if (tid < TW) task_lds[tid] = next_word;
-      ++ti;
-    }
-    __syncthreads();
+    if (finished) ++ti;
   }
 }
 
