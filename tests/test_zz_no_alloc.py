@@ -16,10 +16,10 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 import prefix_shared_tree_amd as pst  # noqa: E402
 
 
-def _pair(spec, **plan_kw):
+def _pair(spec, out_dtype="f32", **plan_kw):
     """Outputs of pst_decode_attn and of pst_decode_attn_noalloc on the same plan."""
     q, k, v = workloads.make_tensors(spec, "cuda")
-    tree = pst.Tree.from_spec(spec, out_dtype="f32")
+    tree = pst.Tree.from_spec(spec, out_dtype=out_dtype)
     plan = pst.Plan(tree, **plan_kw)
     ref, ref_lse = pst.decode_attn(plan, q, k, v)
     out = torch.full_like(ref, float("nan"))
@@ -44,6 +44,15 @@ def test_noalloc_skewed_mqa_and_flattened():
     assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
     ref, ref_lse, out, lse = _pair(workloads.config("3"), flatten=256)
     assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
+
+
+def test_noalloc_bf16_output():
+    # bf16 output: the partials in the array are fp16 with their scales; the
+    # document-QA tree, then the smaller few-shot tree.
+    for name in ("2", "3"):
+        ref, ref_lse, out, lse = _pair(workloads.config(name), out_dtype="bf16")
+        assert out.dtype == torch.bfloat16
+        assert torch.equal(out, ref) and torch.equal(lse, ref_lse), name
 
 
 def test_noalloc_refuses_plans_beyond_its_array():
