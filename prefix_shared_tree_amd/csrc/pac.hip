@@ -37,17 +37,19 @@
 //    straight from the row-major tile with the LDS transpose read
 //    ds_read_b64_tr_b16.  The product O += P V of a tile runs one tile late,
 //    next to the next tile's softmax; for it each V tile is converted once in
-//    LDS to fp16 (scaled by 2^-8) and P is rounded to fp16.  Layouts with two
-//    wavefronts per slab (up to 128 rows, bandwidth-bound) interleave products
-//    and softmax; one slab per wavefront (more rows, compute-bound) issues a
-//    step's products first and tests the lazy maximum per lane;
+//    LDS to fp16, scaled by a power of two chosen per piece from the data,
+//    and P is rounded to fp16.  Layouts with two wavefronts per slab (up to
+//    128 rows, bandwidth-bound) update the row maxima branch-free; one slab
+//    per wavefront (more rows, compute-bound) tests the lazy maximum per lane;
 //  * wavefront dot products (float32, or bf16 pieces below 16 rows on
 //    request): groups of head_dim*elem/16 lanes take one token each, reduce
 //    q.k across the group with DPP, and keep a running (max, sum, O) per row;
 //    states are merged across lane groups and wavefronts at the end.
 // Both use the streaming softmax of CoDec section KV缓存管理 (per-block
 // maximum, rescale of the running sum and numerator at the common maximum)
-// in base 2, and emit the normalised partial O and its natural-log LSE.
+// in base 2, and emit the normalised partial O and its natural-log LSE: in
+// float32, or, for bf16 output, in fp16 scaled by the piece's power of two
+// with the exponent beside the LSE.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
