@@ -121,8 +121,11 @@ typedef struct {
 /* Head layout and dtypes.  head_dim in {64, 128}; num_q_heads a multiple of
  * num_kv_heads; in_dtype PST_F32 or PST_BF16; out_dtype PST_F32 or in_dtype.
  * scale <= 0 means 1/sqrt(head_dim).  Strides in elements; 0 selects the
- * head-major default.  pool_tokens = tokens per head in each pool (0 = the
- * largest kv_offset + kv_len); every node must lie inside it. */
+ * head-major default; strides are multiples of 16 bytes and a token stride
+ * is below 16 MiB.  pool_tokens = tokens per head in each pool (0 = the
+ * largest kv_offset + kv_len); every node must lie inside it, and a paged
+ * pool holds at most 2^31 - 1 tokens per head.  Otherwise
+ * PST_E_INVALID_ARG. */
 typedef struct {
   int32_t num_q_heads;
   int32_t num_kv_heads;

@@ -298,6 +298,18 @@ pst_status pst_tree_build(const pst_tree_desc* desc, const pst_shape* shape, uin
     set_error("K/V strides must be multiples of 16 bytes (128-bit loads)");
     return PST_E_INVALID_ARG;
   }
+  // The kernels address a tile's tokens with 32-bit offsets (up to 128
+  // tokens times the stride) and a paged pool's rows with 32-bit numbers.
+  if (t->shape.kv_stride_token * eb >= (int64_t{1} << 24)) {
+    delete t;
+    set_error("kv_stride_token must be below 16 MiB");
+    return PST_E_INVALID_ARG;
+  }
+  if (t->ix.page_size > 0 && t->pool_tokens > INT32_MAX) {
+    delete t;
+    set_error("a paged pool holds at most 2^31 - 1 tokens per head");
+    return PST_E_INVALID_ARG;
+  }
   if (!(flags & PST_TREE_HOST_ONLY)) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipGetDevice(&t->device);

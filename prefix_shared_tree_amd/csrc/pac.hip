@@ -131,6 +131,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, in
                      (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)))) << 32);
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char*>(u), static_cast<short>(0), n, kBufferWord3);
 }
+// The same for a byte count already known to lie in [0, 2^31).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const char* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t u = static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)))) |
+                     (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)))) << 32);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char*>(u), static_cast<short>(0),
+                                           __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), kBufferWord3);
+}
 
 // One 16-byte-per-lane HBM->LDS DMA: LDS destination = lds_addr + 16 * lane.
 // Written as inline assembly so the compiler does not see an LDS store in
@@ -173,8 +181,12 @@ __device__ __forceinline__ int piece_tid() {
   asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(static_cast<int>(__builtin_amdgcn_workitem_id_x())));
   return t;
 }
+// LDS address of a generic pointer into the LDS: a flat address in the
+// shared aperture holds the aperture base in its upper 32 bits and the LDS
+// address in its lower 32, so truncation gives it.  (A cast to the LDS
+// address space would test the pointer for null on every DMA.)
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
 // Wait until at most n (0..16) of this wavefront's vector memory operations
@@ -259,9 +271,12 @@ __device__ __forceinline__ int page_of(const PacParams& p, const TaskInfo& t, in
   return idx[t.pg0 + ((t.kv_begin + (ft < t.kv_len ? ft : 0)) >> p.page_shift)];
 }
 // Byte offset, from the kv head's first row, of the token ft tokens into the
-// piece, which lies on page `page`.
-__device__ __forceinline__ int64_t paged_off(const PacParams& p, const TaskInfo& t, int64_t stb, int ft, int page) {
-  return ((static_cast<int64_t>(page) << p.page_shift) + ((t.kv_begin + ft) & ((1 << p.page_shift) - 1))) * stb;
+// piece, which lies on page `page`.  32-bit row and stride: the library
+// limits a paged pool to 2^31 - 1 rows and the token stride to 16 MB.
+__device__ __forceinline__ uint64_t paged_off(const PacParams& p, const TaskInfo& t, int64_t stb, int ft, int page) {
+  const uint32_t row = (static_cast<uint32_t>(page) << p.page_shift) |
+                       (static_cast<uint32_t>(t.kv_begin + ft) & ((1u << p.page_shift) - 1u));
+  return static_cast<uint64_t>(row) * static_cast<uint32_t>(stb);
 }
 // Offset of lane `lane`'s chunk of block b inside a descriptor that starts
 // `lead` tokens before the block: token lane / CPT of the block, chunk
@@ -302,8 +317,8 @@ __device__ __forceinline__ void paged_half(const PacParams& p, const TaskInfo& t
   constexpr int TPB = 64 / G::CPT, KB = TILE_BYTES / 1024 / NW;
   const int tok_base = tile * G::TT;
   if (paged_whole_tiles<G::TT>(p, t)) {
-    const int64_t off = paged_off(p, t, stb, tok_base, pg.a);
-    const int64_t bytes = static_cast<int64_t>(min(G::TT, t.kv_len - tok_base)) * stb;
+    const uint64_t off = paged_off(p, t, stb, tok_base, pg.a);
+    const uint32_t bytes = static_cast<uint32_t>(min(G::TT, t.kv_len - tok_base)) * static_cast<uint32_t>(stb);
 #pragma unroll
     for (int c = 0; c < KB; ++c) {
       const int b = c * NW + w;
@@ -313,8 +328,8 @@ __device__ __forceinline__ void paged_half(const PacParams& p, const TaskInfo& t
   }
   const int ft = tok_base + KB * w * TPB;  // the wavefront's first token
   if ((1 << p.page_shift) >= KB * TPB) {
-    const int64_t off = paged_off(p, t, stb, ft, pg.a);
-    const int64_t bytes = static_cast<int64_t>(min(max(t.kv_len - ft, 0), KB * TPB)) * stb;
+    const uint64_t off = paged_off(p, t, stb, ft, pg.a);
+    const uint32_t bytes = static_cast<uint32_t>(min(max(t.kv_len - ft, 0), KB * TPB)) * static_cast<uint32_t>(stb);
 #pragma unroll
     for (int c = 0; c < KB; ++c) emit(off, bytes, block_voff<G::CPT, TPB>(KB * w + c, c * TPB, lane, stb), KB * w + c);
     return;
@@ -322,8 +337,8 @@ __device__ __forceinline__ void paged_half(const PacParams& p, const TaskInfo& t
 #pragma unroll
   for (int c = 0; c < KB; ++c) {
     const int fb = ft + c * TPB;
-    const int64_t off = paged_off(p, t, stb, fb, c == 0 ? pg.a : pg.b);
-    const int64_t bytes = static_cast<int64_t>(min(max(t.kv_len - fb, 0), TPB)) * stb;
+    const uint64_t off = paged_off(p, t, stb, fb, c == 0 ? pg.a : pg.b);
+    const uint32_t bytes = static_cast<uint32_t>(min(max(t.kv_len - fb, 0), TPB)) * static_cast<uint32_t>(stb);
     emit(off, bytes, block_voff<G::CPT, TPB>(KB * w + c, 0, lane, stb), KB * w + c);
   }
 }
@@ -432,17 +447,16 @@ __device__ __forceinline__ void issue_tile(const PacParams& p, const TaskInfo& t
   if (p.page_shift >= 0) {
     // Paged: K and V of a block sit at the same rows.
     const PgPre pg = pg_fetch<D, EB, NW>(p, t, tile, w);
-    paged_half<D, EB, NW>(p, t, stb, tile, lane, w, pg, [&](int64_t off, int64_t bytes, int voff, int b) {
-      dma16(make_rsrc(t.kbase + off, bytes), voff, lds_addr(st + b * 1024));
-      dma16(make_rsrc(t.vbase + off, bytes), voff, lds_addr(st + TILE_BYTES + b * 1024));
+    paged_half<D, EB, NW>(p, t, stb, tile, lane, w, pg, [&](uint64_t off, uint32_t bytes, int voff, int b) {
+      dma16(make_rsrc_n(t.kbase + off, bytes), voff, lds_addr(st + b * 1024));
+      dma16(make_rsrc_n(t.vbase + off, bytes), voff, lds_addr(st + TILE_BYTES + b * 1024));
     });
     return;
   }
-  const char* kb = t.kbase + tok_base * stb;
-  const char* vb = t.vbase + tok_base * stb;
-  const int64_t bytes = static_cast<int64_t>(min(G::TT, t.kv_len - tok_base)) * stb;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, bytes);
+  const uint64_t toff = static_cast<uint64_t>(static_cast<uint32_t>(tok_base)) * static_cast<uint32_t>(stb);
+  const uint32_t bytes = static_cast<uint32_t>(min(G::TT, t.kv_len - tok_base)) * static_cast<uint32_t>(stb);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc_n(t.kbase + toff, bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc_n(t.vbase + toff, bytes);
 #pragma unroll
   for (int c = 0; c < kHalfOps<NW>; ++c) {
     const int b = c * NW + w;
@@ -553,14 +567,16 @@ __device__ __forceinline__ void issue_half(const PacParams& p, const TaskInfo& t
     return;
   }
   if (p.page_shift >= 0) {
-    paged_half<D, 2, NW>(p, t, stb, tile, lane, w, pg, [&](int64_t off, int64_t bytes, int voff, int b) {
-      dma16<NT>(make_rsrc(base + off, bytes), voff, lds_addr(dst + b * 1024));
+    paged_half<D, 2, NW>(p, t, stb, tile, lane, w, pg, [&](uint64_t off, uint32_t bytes, int voff, int b) {
+      dma16<NT>(make_rsrc_n(base + off, bytes), voff, lds_addr(dst + b * 1024));
     });
     return;
   }
-  const char* tbase = base + tok_base * stb;
-  const int64_t bytes = static_cast<int64_t>(min(G::TT, t.kv_len - tok_base)) * stb;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(tbase, bytes);
+  // (tile < nt: at least one token; the library limits the token stride to
+  // 16 MB, so a tile's bytes fit 31 bits.)
+  const char* tbase = base + static_cast<uint64_t>(static_cast<uint32_t>(tok_base)) * static_cast<uint32_t>(stb);
+  const uint32_t bytes = static_cast<uint32_t>(min(G::TT, t.kv_len - tok_base)) * static_cast<uint32_t>(stb);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc_n(tbase, bytes);
 #pragma unroll
   for (int c = 0; c < kHalfOps<NW>; ++c) {
     const int b = c * NW + w;

@@ -142,6 +142,17 @@ def test_unsupported_shape(hq, hkv, d, dt, odt):
             dtype=dt, out_dtype=odt, host_only=True)
 
 
+@pytest.mark.parametrize("stride,ok", [((1 << 22) - 4, True), (1 << 22, False)])
+def test_token_stride_limit(stride, ok):
+    """Token strides of 16 MiB or more are refused (the kernels' per-tile offsets are 32-bit)."""
+    mk = lambda: pst.Tree([-1], [0], [5], [0], num_q_heads=2, num_kv_heads=1, head_dim=64, dtype="f32",
+                          kv_stride_token=stride, kv_stride_head=64, host_only=True)
+    if ok:
+        mk().free()
+    else:
+        _raises("PST_E_INVALID_ARG", mk)
+
+
 def test_bad_cost_tables():
     _raises("PST_E_INVALID_ARG", pst.CostModel, ROWS, LENS, [[0] * 13] * 9)
     bad = _table("affine")
@@ -277,6 +288,7 @@ def test_paged_index_view_and_extent():
     (dict(page_ptr=[0, 2, 4, 6]), "PST_E_INVALID_TREE"),        # node 0: 20 tokens in 2 pages of 8
     (dict(page_idx=[7, 2, -1, 0, 4, 11]), "PST_E_INVALID_TREE"),  # negative page
     (dict(pool_tokens=64), "PST_E_INVALID_TREE"),               # page 11 lies outside 64 rows
+    (dict(pool_tokens=1 << 31), "PST_E_INVALID_ARG"),           # rows beyond 31 bits
 ])
 def test_paged_invalid(kw, code):
     _raises(code, _paged_tree, **kw)
