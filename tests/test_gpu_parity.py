@@ -219,7 +219,7 @@ def test_random_trees(seed):
     check(spec, t, out, lse)
 
 
-@pytest.mark.parametrize("rows", [1, 2, 4, 8, 12, 15, 16, 17, 31, 32, 48, 64, 65, 100, 128, 129, 200, 256])
+@pytest.mark.parametrize("rows", [1, 2, 4, 8, 12, 15, 16, 17, 31, 32, 33, 48, 63, 64, 65, 100, 128, 129, 200, 256])
 def test_row_counts_single_node(rows):
     """One node shared by `rows` MQA rows (g = rows, one query): every row bucket and a ragged tail."""
     spec = workloads.TreeSpec(f"rows{rows}", np.array([-1]), np.array([1000]), np.array([0]), np.array([0]),
@@ -229,7 +229,7 @@ def test_row_counts_single_node(rows):
     check(spec, t, out, lse)
 
 
-@pytest.mark.parametrize("rows", [3, 16, 40, 64, 100, 128, 200, 256])
+@pytest.mark.parametrize("rows", [3, 16, 33, 40, 64, 100, 128, 200, 256])
 def test_row_counts_head_dim_64(rows):
     """Head dim 64: 128-token tiles, so every wavefront runs several 32-token sub-steps per tile."""
     spec = workloads.TreeSpec(f"rows{rows}-d64", np.array([-1]), np.array([1000]), np.array([0]), np.array([0]),
