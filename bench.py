@@ -302,20 +302,25 @@ def decode_loop_bench(torch, pst, workloads, spec, a):
     for name, every, kw in policies:
         sess = DecodeSession(spec, k, v, page_size=P, max_new_tokens=S, replan_every=every, plan_kw=kw)
         torch.cuda.synchronize()
-        gpu = []
+        gpu, dev = [], []
         t0 = time.perf_counter()
         for s in range(S):
+            a0 = torch.cuda.Event(enable_timing=True)
+            a0.record()
             sess.append(kn[s], vn[s])
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             sess.decode(qs[s], out=out, lse=lse)
             e1.record()
             gpu.append((e0, e1))
+            dev.append((a0, e1))
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / S
         results[name] = {
             "wall_ms_per_step": wall * 1e3,
             "gpu_ms_per_step": statistics.mean(x.elapsed_time(y) for x, y in gpu),
+            # the step's device span: the append (new K/V rows, lengths) and PAC + POR
+            "device_ms_per_step": statistics.mean(x.elapsed_time(y) for x, y in dev),
             "replans": sess.replans,
             "replan_ms_each": sess.replan_s * 1e3 / sess.replans if sess.replans else 0.0,
         }
