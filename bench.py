@@ -325,6 +325,17 @@ def decode_loop_bench(torch, pst, workloads, spec, a):
             "replan_ms_each": sess.replan_s * 1e3 / sess.replans if sess.replans else 0.0,
         }
         del sess
+    # The plan-reused loop again without the per-step events (each event is a
+    # marker in the stream that costs device time of its own): wall only.
+    sess = DecodeSession(spec, k, v, page_size=P, max_new_tokens=S)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(S):
+        sess.append(kn[s], vn[s])
+        sess.decode(qs[s], out=out, lse=lse)
+    torch.cuda.synchronize()
+    results["reuse"]["wall_ms_per_step_no_events"] = (time.perf_counter() - t0) * 1e3 / S
+    del sess
     # Tree search: every 8 steps one query finishes and another forks in two,
     # so the batch keeps its size; each fork or finish rebuilds tree and plan.
     per = -(-(1 + S) // P)
