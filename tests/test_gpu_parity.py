@@ -363,6 +363,26 @@ def test_paged_config_sampled(name, P):
     check(spec, (q, k, v), out, lse, queries=sample(spec.num_queries, 16, 11))
 
 
+def test_paged_config5_mha():
+    """The largest workload over 16-token pages: the paged pools hold ~43 GB,
+    so per-head bases lie beyond 2^32 bytes while page rows and tile offsets
+    stay 32-bit; bf16 output (fp16 partials) as the bench runs it.  One query
+    for every fourth node with queries, so every level of the tree is
+    checked."""
+    spec = workloads.config("5-mha")
+    q, k, v = workloads.make_tensors(spec, "cuda")
+    paged, kp, vp = workloads.page_pools(spec, k, v, 16)
+    say(f"config 5-mha paged by 16: {paged['page_ptr'][-1]} pages, pool {kp.shape[1]} rows per head")
+    tree = pst.Tree.from_paged(spec, paged)
+    plan = pst.Plan(tree)
+    out, lse = pst.decode_attn(plan, q, kp, vp)
+    torch.cuda.synchronize()
+    del kp, vp, tree, plan
+    queries = per_leaf_queries(spec)[::4]
+    say(f"  checking {len(queries)} queries")
+    check(spec, (q, k, v), out, lse, queries=queries, by_node=True)
+
+
 FLAT_CASES = [
     # seed, dtype, H_kv, g, d, chunk, page (0 = contiguous), masked fraction, max queries, dot_small
     (0, "bf16", 2, 4, 128, 128, 0, 0.0, 40, False),
